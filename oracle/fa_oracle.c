@@ -1,0 +1,309 @@
+/*
+ * fa_oracle.c -- plain, slow, fp64 CPU oracle for the attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or constant with
+ * the HIP library.
+ *
+ * What it computes is the plain three-step definition of attention, with no
+ * tiling, no online rescaling and no reordering beyond what the definition
+ * states:
+ *
+ *   Page "使用 TileLang 在 AMD GPU 上快速开发高性能 Flash Attention"
+ *   (Fast Flash Attention on AMD GPUs with TileLang), section
+ *   "核心公式与计算流程" (core formulas): scores = Q K^T scaled by 1/sqrt(d),
+ *   an optional lower-triangular causal mask, a softmax over keys, and the
+ *   weighted sum of V.  The formula images are lost from that page; the same
+ *   steps are spelled out in its section "参考实现（PyTorch 版本）"
+ *   (reference implementation): check head counts, repeat K/V heads by the
+ *   group count, Q K^T, divide by sqrt(dim), lower-triangular mask, softmax,
+ *   multiply by V.
+ *
+ *   Mask rule (same page, section "K/V Tile 遍历与核心计算"): a key j is kept
+ *   for query i iff i >= j.
+ *
+ *   Grouped-query heads (same page, section "初始化与Kernel 入口" and the K/V
+ *   loads of "K/V Tile 遍历与核心计算"): head_kv = heads / groups and query
+ *   head h reads K/V head floor(h / groups).
+ *
+ *   Log-sum-exp: the natural log of the softmax denominator of the scaled,
+ *   masked scores of a row, i.e. LSE_i = m_i + ln(sum_j exp(s_ij - m_i)).
+ *   The page "TileLang 与机器学习训练：反向传播算子优化案例" (backward-pass
+ *   case), section on the main backward kernel, consumes it as "lse".
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, o : [B][L][H][D]          (BSHD)
+ *   k, v : [B][L][Hkv][D]
+ *   lse  : [B][H][L]
+ * q/k/v are IEEE binary16 bit patterns, decoded exactly to double.
+ * o and lse are written in double.
+ *
+ * Floating point: every score is a sum over d in ascending order of exact
+ * fp16*fp16 products, in double; exp/log are the C library's double routines.
+ * Compiled without -ffast-math so the summation order is the one written.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* Exact decode of an IEEE 754 binary16 bit pattern to double.
+ * binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * exponent 0  -> subnormal: (-1)^s * 2^-14 * (frac / 1024)
+ * exponent 31 -> inf (frac == 0) or NaN
+ * otherwise   -> (-1)^s * 2^(e-15) * (1 + frac / 1024)                    */
+double fa_oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double mag;
+    if (e == 0) {
+        mag = ldexp((double)frac, -24); /* 2^-14 * frac / 2^10 */
+    } else if (e == 31) {
+        mag = frac == 0 ? INFINITY : NAN;
+    } else {
+        mag = ldexp(1.0 + (double)frac / 1024.0, e - 15);
+    }
+    return sign ? -mag : mag;
+}
+
+/* Decoded value of every binary16 bit pattern, filled once from the decoder
+ * above, so the inner loops do a lookup instead of re-decoding. */
+static double g_half[65536];
+static pthread_once_t g_half_once = PTHREAD_ONCE_INIT;
+
+static void fill_half_table(void)
+{
+    for (uint32_t b = 0; b < 65536u; ++b) g_half[b] = fa_oracle_half_to_double((uint16_t)b);
+}
+
+static double h2d(uint16_t h) { return g_half[h]; }
+
+typedef struct {
+    const uint16_t *q, *k, *v;
+    int B, L, H, Hkv, D, causal;
+    double scale;
+} problem_t;
+
+static size_t q_index(const problem_t *p, int b, int i, int h, int d)
+{
+    return (((size_t)b * p->L + i) * p->H + h) * p->D + d;
+}
+
+static size_t kv_index(const problem_t *p, int b, int j, int hk, int d)
+{
+    return (((size_t)b * p->L + j) * p->Hkv + hk) * p->D + d;
+}
+
+/* Number of keys query i may attend to: all L keys, or keys 0..i under the
+ * causal mask (kept iff i >= j). */
+static int visible_keys(const problem_t *p, int i)
+{
+    return p->causal ? i + 1 : p->L;
+}
+
+/* One output row, straight from the definition.
+ *   s_j  = scale * sum_d Q[b,i,h,d] * K[b,j,hk,d]        for visible j
+ *   m    = max_j s_j
+ *   w_j  = exp(s_j - m),   Z = sum_j w_j
+ *   O_d  = sum_j (w_j / Z) * V[b,j,hk,d]
+ *   LSE  = m + ln Z
+ * `s` is caller-provided scratch of at least L doubles; on return it holds
+ * the probabilities w_j / Z of the visible keys (used by the P export). */
+static void attention_row(const problem_t *p, int b, int h, int i,
+                          double *s, double *o_row, double *lse_out)
+{
+    int groups = p->H / p->Hkv;
+    int hk = h / groups;
+    int n = visible_keys(p, i);
+
+    /* step 1: scaled scores */
+    for (int j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < p->D; ++d)
+            dot += h2d(p->q[q_index(p, b, i, h, d)]) * h2d(p->k[kv_index(p, b, j, hk, d)]);
+        s[j] = p->scale * dot;
+    }
+
+    /* step 2: softmax over the visible keys */
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j)
+        if (s[j] > m) m = s[j];
+    double z = 0.0;
+    for (int j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - m);
+        z += s[j];
+    }
+    for (int j = 0; j < n; ++j)
+        s[j] = s[j] / z;
+
+    /* step 3: weighted sum of V */
+    for (int d = 0; d < p->D; ++d) {
+        double acc = 0.0;
+        for (int j = 0; j < n; ++j)
+            acc += s[j] * h2d(p->v[kv_index(p, b, j, hk, d)]);
+        o_row[d] = acc;
+    }
+    *lse_out = m + log(z);
+}
+
+/* ---------------------------------------------------------------- threads */
+
+typedef struct {
+    const problem_t *p;
+    /* full mode */
+    double *o, *lse;
+    /* rows mode */
+    const int64_t *rows; /* triples (b, h, i) */
+    double *o_rows, *lse_rows;
+    long n_items;
+    long next;
+    pthread_mutex_t lock;
+} job_t;
+
+enum { ROW_CHUNK = 64 };
+
+static long take_item(job_t *job)
+{
+    pthread_mutex_lock(&job->lock);
+    long it = job->next < job->n_items ? job->next++ : -1;
+    pthread_mutex_unlock(&job->lock);
+    return it;
+}
+
+static void *full_worker(void *arg)
+{
+    job_t *job = (job_t *)arg;
+    const problem_t *p = job->p;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(p->L > 0 ? p->L : 1));
+    long chunks = (p->L + ROW_CHUNK - 1) / ROW_CHUNK;
+    long it;
+    while ((it = take_item(job)) >= 0) {
+        long bh = it / chunks, c = it % chunks;
+        int b = (int)(bh / p->H), h = (int)(bh % p->H);
+        int i_end = (int)((c + 1) * ROW_CHUNK < p->L ? (c + 1) * ROW_CHUNK : p->L);
+        for (int i = (int)(c * ROW_CHUNK); i < i_end; ++i)
+            attention_row(p, b, h, i, s, job->o + q_index(p, b, i, h, 0),
+                          job->lse + ((size_t)b * p->H + h) * p->L + i);
+    }
+    free(s);
+    return NULL;
+}
+
+static void *rows_worker(void *arg)
+{
+    job_t *job = (job_t *)arg;
+    const problem_t *p = job->p;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(p->L > 0 ? p->L : 1));
+    long it;
+    while ((it = take_item(job)) >= 0) {
+        const int64_t *r = job->rows + 3 * it;
+        attention_row(p, (int)r[0], (int)r[1], (int)r[2], s,
+                      job->o_rows + (size_t)it * p->D, job->lse_rows + it);
+    }
+    free(s);
+    return NULL;
+}
+
+static int resolve_threads(int nthreads)
+{
+    if (nthreads > 0) return nthreads;
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+static void run_pool(job_t *job, void *(*fn)(void *), int nthreads)
+{
+    int n = resolve_threads(nthreads);
+    if (n > job->n_items) n = (int)(job->n_items > 0 ? job->n_items : 1);
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n);
+    pthread_mutex_init(&job->lock, NULL);
+    job->next = 0;
+    for (int t = 0; t < n; ++t) pthread_create(&tid[t], NULL, fn, job);
+    for (int t = 0; t < n; ++t) pthread_join(tid[t], NULL);
+    pthread_mutex_destroy(&job->lock);
+    free(tid);
+}
+
+/* Returns 0 on success, -1 on invalid arguments (the oracle checks only what
+ * it needs to stay in bounds: H divisible by Hkv, positive sizes). */
+static int check_problem(int B, int L, int H, int Hkv, int D)
+{
+    pthread_once(&g_half_once, fill_half_table);
+    if (B < 0 || L < 0 || H <= 0 || Hkv <= 0 || D <= 0) return -1;
+    if (H % Hkv != 0) return -1;
+    return 0;
+}
+
+/* Whole forward: o [B][L][H][D], lse [B][H][L] (lse may be NULL).
+ * Work is split over (b, h, 64-row chunk) among `nthreads` POSIX threads
+ * (0 = all online cores); each row is computed independently, so the thread
+ * count never changes a result. */
+int fa_oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  double *o, double *lse, int B, int L, int H, int Hkv, int D,
+                  int causal, double scale, int nthreads)
+{
+    if (check_problem(B, L, H, Hkv, D)) return -1;
+    problem_t p = {q, k, v, B, L, H, Hkv, D, causal ? 1 : 0, scale};
+    double *lse_buf = lse;
+    if (!lse_buf) lse_buf = (double *)malloc(sizeof(double) * ((size_t)B * H * L + 1));
+    job_t job;
+    memset(&job, 0, sizeof(job));
+    job.p = &p;
+    job.o = o;
+    job.lse = lse_buf;
+    job.n_items = (long)B * H * ((L + ROW_CHUNK - 1) / ROW_CHUNK);
+    if (job.n_items > 0) run_pool(&job, full_worker, nthreads);
+    if (!lse) free(lse_buf);
+    return 0;
+}
+
+/* Selected rows only: rows holds n_rows triples (b, h, i); o_rows is
+ * [n_rows][D], lse_rows is [n_rows].  Same arithmetic as fa_oracle_fwd, so a
+ * sampled row equals the corresponding full-forward row bit for bit. */
+int fa_oracle_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   int B, int L, int H, int Hkv, int D, int causal, double scale,
+                   const int64_t *rows, long n_rows, double *o_rows,
+                   double *lse_rows, int nthreads)
+{
+    if (check_problem(B, L, H, Hkv, D)) return -1;
+    for (long r = 0; r < n_rows; ++r) {
+        const int64_t *t = rows + 3 * r;
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= L)
+            return -1;
+    }
+    problem_t p = {q, k, v, B, L, H, Hkv, D, causal ? 1 : 0, scale};
+    job_t job;
+    memset(&job, 0, sizeof(job));
+    job.p = &p;
+    job.rows = rows;
+    job.o_rows = o_rows;
+    job.lse_rows = lse_rows;
+    job.n_items = n_rows;
+    if (n_rows > 0) run_pool(&job, rows_worker, nthreads);
+    return 0;
+}
+
+/* Softmax probabilities of one row: probs[j] for j < L, zero for masked keys.
+ * Exposed so tests can check that each row of the softmax sums to one. */
+int fa_oracle_row_probs(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int B, int L, int H, int Hkv, int D, int causal,
+                        double scale, int b, int h, int i, double *probs)
+{
+    if (check_problem(B, L, H, Hkv, D)) return -1;
+    if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= L) return -1;
+    problem_t p = {q, k, v, B, L, H, Hkv, D, causal ? 1 : 0, scale};
+    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    double *o_row = (double *)malloc(sizeof(double) * (size_t)D);
+    double lse;
+    attention_row(&p, b, h, i, s, o_row, &lse);
+    int n = visible_keys(&p, i);
+    for (int j = 0; j < L; ++j) probs[j] = j < n ? s[j] : 0.0;
+    free(s);
+    free(o_row);
+    return 0;
+}
