@@ -1,0 +1,187 @@
+"""Throughput of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one fa_fwd call (the whole forward: work decomposition, Q/K/V
+tiles, both products, online softmax, normalisation, O and LSE stores) over
+the workload's seeded synthetic inputs, already resident in HBM.  Prints one
+JSON line on stdout; extra detail goes to stderr.
+
+Default workload: B=8, H=32, L=4096, D=128, non-causal -- the shape the
+throughput target is quoted on.  FLOPs = 4*B*H*L^2*D (halved when causal).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·L²·D, causal halved) + % of MFMA FP16 peak"
+PEAK_FP16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
+KERNEL_SRC = os.path.join(ROOT, "tiled_attention_flash_amd", "csrc", "fa_fwd_kernel.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, valid
+    only while the kernel source is the one the counters were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("kernel_sha") != kernel_sha():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(w, q, k, v, target_s: float):
+    """The fp64 oracle timed on the host on a bounded sample of the same
+    workload: whole output rows, the first ones of every (b, h) in turn."""
+    import numpy as np
+
+    import oracle
+
+    threads = cpu_threads()
+
+    def row_ids(n):
+        rng = np.random.default_rng(0)
+        b = rng.integers(0, w.B, n)
+        h = rng.integers(0, w.H, n)
+        i = rng.integers(0, w.L, n)
+        return np.stack([b, h, i], axis=1)
+
+    def flops(ids):
+        if not w.causal:
+            return 4.0 * w.L * w.D * len(ids)
+        return float(sum(4.0 * (int(i) + 1) * w.D for i in ids[:, 2]))
+
+    ids = row_ids(threads * 8)
+    t0 = time.perf_counter()
+    oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads)
+    probe = time.perf_counter() - t0
+    n = int(max(threads, min(2_000_000, len(ids) * target_s / max(probe, 1e-6))))
+    ids = row_ids(n)
+    t0 = time.perf_counter()
+    oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": flops(ids) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} random output rows (b, h, i) of the same inputs, fp64, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: the forward pass here is a single-GPU kernel "
+              "and no multi-GPU path is built (see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import tiled_attention_flash_amd as fa
+    from tiled_attention_flash_amd.inputs import HEADLINE, WORKLOADS, workload_inputs
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = workload_inputs(w, seed=args.seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # timed region: one event pair per launch (kernel duration) inside one
+    # bracketing pair (whole-job time), all on the stream the kernel runs on
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize(dev)
+    total_ms = t_begin.elapsed_time(t_end)
+    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    kernel_ms = sum(per_launch) / len(per_launch)
+    ms_per_step = total_ms / args.steps
+
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    traffic = measured_traffic(name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "L": w.L, "D": w.D,
+                   "causal": w.causal, "layout": "BSHD", "seed": args.seed},
+        "pct_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": traffic},
+        "kernel_ms_mean": round(kernel_ms, 5),
+        "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
+        "kernel_sha": kernel_sha(),
+    }
+    print(f"[bench] {name}: {ms_per_step:.4f} ms/step, kernel {kernel_ms:.4f} ms, "
+          f"{value:.1f} TFLOP/s ({result['pct_peak']}% of {PEAK_FP16_TFLOPS})",
+          file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

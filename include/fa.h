@@ -1,0 +1,94 @@
+/*
+ * fa.h -- C ABI of libfa.so, the attention forward pass for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Operation (page "使用 TileLang 在 AMD GPU 上快速开发高性能 Flash Attention",
+ * sections "核心公式与计算流程" and "K/V Tile 遍历与核心计算"):
+ *
+ *   for every batch b, query head h and query row i:
+ *     hk    = h / (H / Hkv)                         grouped-query K/V head
+ *     s_j   = scale * sum_d Q[b,i,h,d] * K[b,j,hk,d]  for visible keys j
+ *             (all j < L; with causal != 0 only j <= i)
+ *     O[b,i,h,:] = sum_j softmax_j(s) * V[b,j,hk,:]
+ *     LSE[b,h,i] = ln( sum_j exp(s_j) )             natural log, scaled scores
+ *
+ * computed tile by tile with an fp32 online softmax (running row maximum,
+ * running row sum, rescaled fp32 output accumulator), fp16 inputs, fp16
+ * probabilities into the second product, fp32 accumulation, and the output
+ * rounded to fp16 with round-to-nearest-even.
+ *
+ * The library allocates nothing, keeps no per-call state and never
+ * synchronises the device: every call only validates its arguments and
+ * enqueues kernels on `stream`.  It is reentrant and thread-safe.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef FA_API
+#define FA_API __attribute__((visibility("default")))
+#endif
+
+/* Same definition as the HIP runtime's own handle type, so this header does
+ * not need the HIP headers. 0 (NULL) is the null stream. */
+typedef struct ihipStream_t *hipStream_t;
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULLPTR = 1,  /* q, k, v or o is NULL                                  */
+    FA_ERR_SHAPE = 2,    /* B, L, H, Hkv or D negative, or a size overflows int64  */
+    FA_ERR_GQA = 3,      /* Hkv <= 0, H <= 0, or H not a multiple of Hkv           */
+    FA_ERR_HEADDIM = 4,  /* D is not 64 or 128                                     */
+    FA_ERR_SCALE = 5,    /* scale is not finite or not > 0                         */
+    FA_ERR_ALIGN = 6,    /* a tensor pointer is not 16-byte aligned (lse: 4-byte)  */
+    FA_ERR_ALIAS = 7,    /* the byte range of o or lse overlaps q, k, v or each other */
+    FA_ERR_LAUNCH = 8,   /* the HIP runtime rejected the launch                    */
+    FA_ERR_DEVICE = 9    /* the current device could not be queried                */
+};
+
+/*
+ * fa_fwd -- attention forward pass.
+ *
+ * q    device pointer, fp16 (IEEE binary16), contiguous [B][L][H][D]   (read)
+ * k    device pointer, fp16, contiguous [B][L][Hkv][D]                 (read)
+ * v    device pointer, fp16, contiguous [B][L][Hkv][D]                 (read)
+ * o    device pointer, fp16, contiguous [B][L][H][D]                   (written)
+ * lse  device pointer, fp32, contiguous [B][H][L], or NULL to skip it  (written)
+ *      LSE[b,h,i] = ln sum_{visible j} exp(s_ij), with s_ij the scaled score.
+ * B, L, H, Hkv, D   batch, sequence length (queries = keys), query heads,
+ *      K/V heads (H % Hkv == 0; query head h uses K/V head h / (H/Hkv)),
+ *      head dimension (64 or 128).
+ * causal  nonzero: key j is visible to query i iff j <= i (top-left aligned,
+ *      which is also bottom-right aligned because queries and keys have the
+ *      same length).
+ * scale   multiplier of Q.K; must be finite and > 0 (1/sqrt(D) is the usual).
+ * stream  HIP stream the kernels are enqueued on.
+ *
+ * Ownership: the caller allocates and frees every buffer; they must stay
+ * valid until the enqueued work has completed.  o and lse must not overlap
+ * q, k, v or each other (checked on the pointers' byte ranges).
+ *
+ * Returns FA_OK once the work is enqueued, or an fa_status error, in which
+ * case nothing was launched and no buffer was touched.  All argument checks
+ * happen before any HIP call.  B == 0 or L == 0 returns FA_OK and launches
+ * nothing.  Faults inside the kernel surface at the caller's next
+ * synchronisation on `stream`.
+ */
+FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int L, int H, int Hkv, int D, int causal, float scale,
+           hipStream_t stream);
+
+/* Human-readable name of an fa_status value (static storage, never NULL). */
+FA_API const char *fa_status_string(int status);
+
+/* Version of this ABI (bumped when a signature or a layout changes). */
+FA_API int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,92 @@
+"""The C ABI of libfa.so, on the host: it loads, exports every symbol that
+include/fa.h declares, and rejects every invalid argument with the documented
+status before any HIP call (fake, never-dereferenced addresses are passed, so
+a launch would be a bug)."""
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_attention_flash_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# fake device addresses, 256-byte aligned, far apart (never dereferenced)
+Q, K, V, O, LSE = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+OK_ARGS = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=1, L=128, H=2, Hkv=2, D=64, causal=0,
+               scale=0.125, stream=None)
+
+
+def call(**kw):
+    a = dict(OK_ARGS)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["L"], a["H"], a["Hkv"],
+                     a["D"], a["causal"], a["scale"], a["stream"])
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"^FA_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = fa.library()
+    names = declared_symbols()
+    assert set(names) == {"fa_fwd", "fa_status_string", "fa_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], check=True,
+                         stdout=subprocess.PIPE, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    # nothing beyond the declared C ABI leaks out of the library
+    assert exported == set(names)
+    assert lib.fa_abi_version() == 1
+
+
+def test_status_strings():
+    for code, name in fa.STATUS.items():
+        assert fa.fa_status_string(code).startswith(name)
+    assert fa.fa_status_string(12345) == "FA_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=-1), 2), (dict(L=-5), 2), (dict(D=-64), 2), (dict(H=-2), 2),
+    (dict(B=1 << 30, L=1 << 30, H=1 << 30, Hkv=1 << 30, D=128), 2),
+    (dict(H=3, Hkv=2), 3), (dict(Hkv=0), 3), (dict(H=0), 3), (dict(H=4, Hkv=8), 3),
+    (dict(D=96), 4), (dict(D=32), 4), (dict(D=256), 4), (dict(D=0), 4),
+    (dict(scale=0.0), 5), (dict(scale=-0.125), 5), (dict(scale=math.nan), 5),
+    (dict(scale=math.inf), 5),
+    (dict(q=Q + 8), 6), (dict(k=K + 2), 6), (dict(v=V + 4), 6), (dict(o=O + 1), 6),
+    (dict(lse=LSE + 2), 6),
+    (dict(o=Q), 7), (dict(o=K + 64), 7), (dict(lse=V + 256), 7), (dict(lse=O + 16), 7),
+    (dict(o=Q - 1024), 7),
+])
+def test_invalid_arguments_rejected_without_launch(kw, status):
+    assert call(**kw) == status
+
+
+def test_empty_problems_are_noops():
+    assert call(B=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert call(L=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    # still validated
+    assert call(B=0, D=96) == 4
+    assert call(L=0, H=3, Hkv=2) == 3
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        fa.forward(q, q, q)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        fa.library()

@@ -1,0 +1,202 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Bar (all absolute, over every compared element):
+    max |O_gpu - O_ref| <= 1e-2,  mean |O_gpu - O_ref| <= 1e-3,
+    max |LSE_gpu - LSE_ref| <= 1e-3.
+
+* Small shapes (the oracle computes every row in seconds): the tiny workload,
+  ragged lengths around the 64-key tile and 128-query block edges, every
+  grouped-query ratio, both head dims, causal and not -- compared element by
+  element.
+* The full-size workloads, in the same launch configuration the benchmark
+  times: rows sampled where errors would show (first/last rows, q-block and
+  key-tile edges, the diagonal neighbourhood, random rows over every head),
+  each computed by the oracle one by one; plus properties that hold at any
+  size (finite output, output inside the range of V, causal row 0 == V[0]
+  exactly, bitwise determinism).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_attention_flash_amd as fa
+from tiled_attention_flash_amd.inputs import WORKLOADS, make_qkv, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_O, MEAN_O, MAX_LSE = 1e-2, 1e-3, 1e-3
+
+
+def gpu_forward(q, k, v, causal, scale=None):
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
+    d = np.abs(o_gpu.double().numpy() - o_ref)
+    dl = np.abs(lse_gpu.double().numpy() - lse_ref)
+    msg = f"{what}: max|dO|={d.max():.3e} mean|dO|={d.mean():.3e} max|dLSE|={dl.max():.3e}"
+    print(msg, flush=True)
+    assert d.max() <= MAX_O, msg
+    assert d.mean() <= MEAN_O, msg
+    assert dl.max() <= MAX_LSE, msg
+
+
+def full_case(B, L, H, Hkv, D, causal, seed, qk_mult=1.0):
+    q, k, v = make_qkv(B, L, H, Hkv, D, seed=seed, qk_mult=qk_mult)
+    o_ref, lse_ref = oracle.forward(q, k, v, causal=causal)
+    o, lse = gpu_forward(q, k, v, causal)
+    assert_close(o, lse, o_ref, lse_ref, f"B{B} L{L} H{H} Hkv{Hkv} D{D} causal={causal} seed={seed}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_workload(seed, causal):
+    w = WORKLOADS["tiny-mha-L128-d64"]
+    full_case(w.B, w.L, w.H, w.Hkv, w.D, causal, seed)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("L", [1, 3, 63, 64, 65, 100, 127, 128, 129, 200, 1000])
+def test_ragged_lengths(L, D, causal):
+    full_case(1, L, 2, 1, D, causal, seed=L)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("groups", [1, 2, 4, 8])
+def test_gqa_ratios(groups, causal):
+    full_case(2, 257, 8, 8 // groups, 128, causal, seed=30 + groups)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_multi_block(D, causal):
+    full_case(2, 640, 4, 2, D, causal, seed=40 + D)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_logits(causal):
+    # the long-sequence workload's input range (Q, K x 3) on a short sequence
+    full_case(1, 512, 4, 4, 128, causal, seed=50, qk_mult=3.0)
+
+
+def test_nondefault_scale():
+    q, k, v = make_qkv(1, 300, 2, 2, 64, seed=60)
+    for scale in (0.03, 0.5):
+        o_ref, lse_ref = oracle.forward(q, k, v, causal=True, scale=scale)
+        o, lse = gpu_forward(q, k, v, True, scale=scale)
+        assert_close(o, lse, o_ref, lse_ref, f"scale={scale}")
+
+
+# ------------------------------------------------------- full-size workloads
+
+def sample_rows(B, H, L, seed, n_random=96):
+    rng = np.random.default_rng(seed)
+    edges = sorted({0, 1, 63, 64, 65, 127, 128, 129, L // 2, L - 129, L - 128, L - 65, L - 64,
+                    L - 2, L - 1})
+    edges = [i for i in edges if 0 <= i < L]
+    rows = []
+    for n, i in enumerate(edges):
+        rows.append((n % B, (7 * n) % H, i))
+    for _ in range(n_random):
+        rows.append((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(L))))
+    for h in range(H):  # every head at least once
+        rows.append((h % B, h, int(rng.integers(L))))
+    return np.array(rows, dtype=np.int64)
+
+
+FULL = ["mha-b8-h32-L1024-d64", "mha-b8-h32-L1024-d64-causal", "mha-b8-h32-L4096-d128",
+        "mha-b8-h32-L4096-d128-causal", "gqa-b2-h32-kv8-L8192-d128-causal",
+        "mha-b1-h32-L16384-d128-causal-qk3"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    w = WORKLOADS[name]
+    print(f"workload {name}", flush=True)
+    q, k, v = workload_inputs(w, seed=0)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o1, lse1 = fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale)
+    o2, lse2 = fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    # bitwise determinism
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
+    # finite; every output inside the range of V (a convex combination of V rows)
+    assert torch.isfinite(o1).all() and torch.isfinite(lse1).all()
+    vmin, vmax = vd.min().float(), vd.max().float()
+    assert o1.float().min() >= vmin - 1e-2 and o1.float().max() <= vmax + 1e-2
+    if w.causal:  # row 0 sees only key 0: probability exactly 1
+        g = w.H // w.Hkv
+        assert torch.equal(o1[:, 0], vd[:, 0].repeat_interleave(g, dim=1))
+    ids = sample_rows(w.B, w.H, w.L, seed=1)
+    o_ref, lse_ref = oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale)
+    oc, lc = o1.cpu(), lse1.cpu()
+    o_got = torch.stack([oc[b, i, h] for b, h, i in ids])
+    l_got = torch.stack([lc[b, h, i] for b, h, i in ids])
+    assert_close(o_got, l_got, o_ref, lse_ref, f"{name} ({len(ids)} sampled rows)")
+
+
+# ------------------------------------------------------------- properties
+
+def test_gqa_equals_repeated_mha_bitwise():
+    q, k, v = make_qkv(2, 1024, 32, 8, 128, seed=70)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for causal in (False, True):
+        o1, l1 = fa.forward(qd, kd, vd, causal=causal)
+        o2, l2 = fa.forward(qd, kd.repeat_interleave(4, dim=2).contiguous(),
+                            vd.repeat_interleave(4, dim=2).contiguous(), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_lse_optional_and_side_streams():
+    q, k, v = make_qkv(2, 777, 4, 2, 64, seed=80)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = fa.forward(qd, kd, vd, causal=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o2, l2 = fa.forward(qd, kd, vd, causal=True, with_lse=False)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert l2 is None
+    assert torch.equal(o1, o2)
+
+
+def test_adjacent_output_buffer_and_preallocated_outputs():
+    q, k, v = make_qkv(1, 256, 2, 2, 128, seed=90)
+    n = q.numel()
+    pool = torch.empty(2 * n, dtype=torch.float16, device="cuda")
+    pool[:n].copy_(q.view(-1).cuda())
+    qd = pool[:n].view(q.shape)
+    out = pool[n:].view(q.shape)  # starts exactly where q ends
+    lse = torch.full((1, 2, 256), float("nan"), device="cuda")
+    o, l = fa.forward(qd, k.cuda(), v.cuda(), causal=False, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr() and l.data_ptr() == lse.data_ptr()
+    assert torch.equal(pool[:n].view(q.shape).cpu(), q)  # input untouched
+    o_ref, lse_ref = oracle.forward(q, k, v, causal=False)
+    assert_close(o.cpu(), l.cpu(), o_ref, lse_ref, "adjacent buffers")
+
+
+def test_empty_inputs():
+    z = torch.empty((0, 16, 2, 64), dtype=torch.float16, device="cuda")
+    o, l = fa.forward(z, z, z)
+    assert o.shape == z.shape and l.shape == (0, 2, 16)
+    z = torch.empty((1, 0, 2, 64), dtype=torch.float16, device="cuda")
+    o, l = fa.forward(z, z, z, causal=True)
+    assert o.shape == z.shape and l.shape == (1, 2, 0)
+
+
+def test_binding_reports_misaligned_view():
+    q, k, v = make_qkv(1, 64, 1, 1, 64, seed=91)
+    flat = torch.zeros(q.numel() + 8, dtype=torch.float16, device="cuda")
+    qm = flat[1:1 + q.numel()].view(q.shape)  # 2-byte offset
+    with pytest.raises(fa.FaError) as e:
+        fa.forward(qm, k.cuda(), v.cuda())
+    assert e.value.status == 6

@@ -1,0 +1,110 @@
+"""Attention forward pass for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over ``libfa.so`` (C ABI declared in ``include/fa.h``):
+argument marshalling only; every step of the computation runs in the HIP
+kernels.  PyTorch supplies device memory and the current stream.
+
+    o, lse = tiled_attention_flash_amd.forward(q, k, v, causal=False, scale=None)
+
+q ``[B, L, H, D]``, k/v ``[B, L, Hkv, D]``: contiguous fp16 tensors on the
+current HIP device (BSHD layout), D in {64, 128}, H a multiple of Hkv.
+Returns o ``[B, L, H, D]`` fp16 and lse ``[B, H, L]`` fp32 (natural-log
+log-sum-exp of each row's scaled scores).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["forward", "fa_fwd", "fa_status_string", "library", "library_path", "FaError",
+           "STATUS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa.so")
+_lib = None
+
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_SHAPE", 3: "FA_ERR_GQA", 4: "FA_ERR_HEADDIM",
+    5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_LAUNCH",
+    9: "FA_ERR_DEVICE",
+}
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """Load libfa.so.  There is no fallback: a missing library is an error."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m tiled_attention_flash_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp = ctypes.c_void_p
+    c_int = ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 6 + [ctypes.c_float, vp]
+    lib.fa_fwd.restype = c_int
+    lib.fa_status_string.argtypes = [c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = c_int
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return library().fa_status_string(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, L, H, Hkv, D, causal, scale, stream) -> int:
+    """Direct call of the C entry point with raw addresses (ints or None).
+    Returns the status code unchanged."""
+    return int(library().fa_fwd(q, k, v, o, lse, int(B), int(L), int(H), int(Hkv), int(D),
+                                int(bool(causal)), float(scale), stream))
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            with_lse: bool = True):
+    """Attention forward on the current stream.  Returns (o, lse); lse is None
+    when ``with_lse`` is False and no ``lse`` buffer is given."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float16 tensor on a HIP device")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D [B, L, heads, D] tensor")
+    B, L, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != L or k.shape[3] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous float16 tensor shaped like q on q's device")
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, H, L) or lse.dtype != torch.float32 or
+                              not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, L] tensor on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd(q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
+                    out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
+                    B, L, H, Hkv, D, causal, scale, stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out, lse

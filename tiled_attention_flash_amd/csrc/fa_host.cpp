@@ -1,0 +1,81 @@
+// fa_host.cpp -- the C-ABI front end of libfa.so: argument validation and
+// dispatch.  Every check runs before any HIP call, so a rejected call never
+// touches the device (and the checks can be exercised on a host without one).
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool mul_overflows(int64_t a, int64_t b, int64_t *out) { return __builtin_mul_overflow(a, b, out); }
+
+// Element count of a 4-D tensor, or -1 on int64 overflow.
+int64_t elems4(int a, int b, int c, int d)
+{
+    int64_t x;
+    if (mul_overflows(a, b, &x) || mul_overflows(x, c, &x) || mul_overflows(x, d, &x)) return -1;
+    return x;
+}
+
+bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
+{
+    if (!a || !b || a_bytes <= 0 || b_bytes <= 0) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+bool misaligned(const void *p, uintptr_t to) { return ((uintptr_t)p & (to - 1)) != 0; }
+
+}  // namespace
+
+extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                      int L, int H, int Hkv, int D, int causal, float scale, hipStream_t stream)
+{
+    if (B < 0 || L < 0 || H < 0 || Hkv < 0 || D < 0) return FA_ERR_SHAPE;
+    if (H <= 0 || Hkv <= 0 || H % Hkv != 0) return FA_ERR_GQA;
+    if (D != 64 && D != 128) return FA_ERR_HEADDIM;
+    if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+
+    int64_t q_elems = elems4(B, L, H, D);
+    int64_t kv_elems = elems4(B, L, Hkv, D);
+    int64_t lse_elems = elems4(B, H, L, 1);
+    if (q_elems < 0 || kv_elems < 0 || lse_elems < 0 || q_elems > INT64_MAX / 4)
+        return FA_ERR_SHAPE;
+    if (B == 0 || L == 0) return FA_OK;  // nothing to compute; pointers may be null
+
+    if (!q || !k || !v || !o) return FA_ERR_NULLPTR;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(lse, 4))
+        return FA_ERR_ALIGN;
+
+    const int64_t q_bytes = q_elems * 2, kv_bytes = kv_elems * 2, lse_bytes = lse_elems * 4;
+    if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) ||
+        overlaps(o, q_bytes, v, kv_bytes) || overlaps(o, q_bytes, lse, lse_bytes) ||
+        overlaps(lse, lse_bytes, q, q_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
+        overlaps(lse, lse_bytes, v, kv_bytes))
+        return FA_ERR_ALIAS;
+
+    fa::Problem p{q, k, v, o, lse, B, L, H, Hkv, D, causal != 0, scale};
+    return fa::launch_forward(p, stream);
+}
+
+extern "C" const char *fa_status_string(int status)
+{
+    switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULLPTR: return "FA_ERR_NULLPTR: q, k, v or o is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative size or size overflow";
+    case FA_ERR_GQA: return "FA_ERR_GQA: H and Hkv must be positive and H a multiple of Hkv";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o need 16-byte, lse 4-byte alignment";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: o or lse overlaps another tensor";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
+    case FA_ERR_DEVICE: return "FA_ERR_DEVICE: could not query the current device";
+    default: return "FA_ERR_UNKNOWN";
+    }
+}
+
+extern "C" int fa_abi_version(void) { return 1; }
