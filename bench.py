@@ -99,6 +99,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB "
+                         "`--steps` times (the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -108,6 +111,17 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.float16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n,
+                          "launches": args.steps}), flush=True)
+        return 0
 
     import tiled_attention_flash_amd as fa
     from tiled_attention_flash_amd.inputs import HEADLINE, WORKLOADS, workload_inputs

@@ -14,24 +14,34 @@
 // * Workgroup = 4 wavefronts (256 lanes) owning one block of BM = 128 query
 //   rows of one (batch, query head); each wavefront owns 32 whole query rows.
 // * Both products are computed transposed, on v_mfma_f32_32x32x16_f16:
-//     S^T[key][query]  = K . Q^T     (A = K rows from LDS, B = Q from VGPRs)
-//     O^T[d][query]   += V^T . P^T   (A = V^T from LDS,    B = P from VGPRs)
-//   In the 32x32 accumulator layout lane l holds column l%32, i.e. one query,
-//   and 16 of its 32 rows (keys, or d) -- the other 16 live in lane l^32.
-//   Row statistics are therefore per-lane values plus ONE exchange between
-//   the two 32-lane halves (v_permlane32_swap), and the per-row rescale of
-//   O^T is a per-lane scalar.
-// * The S^T accumulator registers, converted to fp16, are exactly the B
-//   operand of the second product once the 16 keys of each k-step are taken
-//   in the order the accumulator holds them; V^T is stored in LDS in that
-//   same key order, so P never leaves registers.
-// * K/V tiles of BN = 64 keys: 128-bit coalesced global loads into registers
-//   one tile ahead, then stored to a double-buffered LDS tile (K row-major
-//   with a 16-byte row pad, V transposed with an XOR-swizzled 16-byte chunk
-//   order) -- one workgroup barrier per tile.
+//     S^T[key][query]  = K . Q^T     (A = K rows from LDS, B = Q in VGPRs)
+//     O^T[d][query]   += V^T . P^T   (A = V^T from LDS,   B = P in VGPRs)
+//   In the 32x32 accumulator layout lane l holds column l%32 -- one query --
+//   and 16 of its 32 rows (keys, or d); the other 16 live in lane l^32.  Row
+//   statistics are per-lane values plus ONE exchange between the two 32-lane
+//   halves (v_permlane32_swap), and the per-row rescale of O^T is a per-lane
+//   scalar.
+// * The S^T accumulators, converted to fp16, are the B operand of the second
+//   product once the 16 keys of each k-step are taken in the order the
+//   accumulator holds them (lane half h: keys 4h..4h+3, then 8+4h..8+4h+3).
+//   V stays row-major in LDS and ds_read_b64_tr_b16 (which hands lane i of a
+//   16-lane group column i of the 4x16 block its group points at) builds the
+//   V^T operand in exactly that key order, so P never leaves registers.
+// * K/V tiles of BN = 64 keys travel HBM -> LDS with global_load_lds_dwordx4
+//   (16 bytes per lane, no staging registers), double-buffered, one
+//   workgroup barrier per tile.  The source address of each lane is chosen so
+//   that rows land with a 16-byte-chunk XOR swizzle that makes the K reads
+//   (ds_read_b128, 16 rows per LDS cycle) and the V transpose reads (4 rows x
+//   64 bytes per half-wavefront) free of bank conflicts.  Rows past the end of
+//   the sequence load row L-1 instead (finite data that the mask hides).
+// * Online softmax with a lazy rescale: the reference maximum of a row is
+//   raised (and O, l rescaled) only when some row of the wavefront sees its
+//   maximum grow by more than 2^8 in the exp2 domain; otherwise the stale
+//   maximum keeps every probability <= 256 (exact in fp16's range) and the
+//   final O / l and LSE are unchanged.
 // * Causal: tiles past the block's last query are never visited; the mask
-//   code runs only on tiles that straddle a wavefront's diagonal (or hold
-//   the ragged end of the sequence).
+//   code runs only on tiles that straddle a wavefront's diagonal (or hold the
+//   ragged end of the sequence).
 // * Grid: one workgroup per (b, kv head, group member, q block) work item;
 //   workgroup ids are remapped so that each of the 8 XCDs (which receive
 //   workgroups round-robin) walks a contiguous range of work items, keeping
@@ -47,16 +57,18 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float float2v __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per work item
 constexpr int kBN = 64;           // keys per K/V tile
 constexpr int kXcds = 8;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
 
 struct Args {
     const _Float16 *q, *k, *v;
@@ -71,9 +83,8 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // v_permlane32_swap exchanges the upper half of one register with the lower
 // half of another; given the same value twice, each lane ends up holding its
-// own value in one result and lane l^32's value in the other.  Combining the
-// two symmetrically gives the cross-half max / sum without caring which is
-// which.
+// own value in one result and lane l^32's value in the other, so a symmetric
+// combination of the two is the cross-half max / sum.
 __device__ __forceinline__ float pair_max(float x)
 {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -86,116 +97,98 @@ __device__ __forceinline__ float pair_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position, inside a tile of kBN keys, at which V^T stores key `key` so that
-// a 16-byte LDS read returns the 8 keys lane-half `h` of the k-step needs:
-// k-step c covers keys 16c..16c+15; the accumulator holds, for lane half h,
-// keys 16c + {4h..4h+3, 8+4h..8+4h+3} in that order.
-__device__ __forceinline__ int vt_position(int key)
+// Tile geometry.  A tile row is D halves = D/8 chunks of 16 bytes.
+template <int D>
+struct Geo {
+    static constexpr int kChunks = D / 8;               // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kChunks;   // rows one wave load instruction fills
+    static constexpr int kLoadsPerTile = kBN / kRowsPerLoad;
+    static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
+    static constexpr int kTile = kBN * D;               // halves per K (or V) tile
+    static_assert(kLoadsPerTile % kWaves == 0, "tile loads must split over the waves");
+};
+
+// Physical 16-byte chunk of logical chunk `c` of K row `row`: 16 consecutive
+// rows read at one logical chunk hit 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_chunk(int row, int c)
 {
-    int c = key >> 4, r = key & 15;
-    int a = r >> 3, h = (r >> 2) & 1, j = r & 3;
-    return 16 * c + 8 * h + 4 * a + j;
+    return D == 128 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
 }
 
-// 16-byte chunk swizzle of V^T rows (kBN = 64 halves = 8 chunks per row): a
-// 16-byte read by 16 consecutive rows, and by 8 consecutive rows, touches
-// every LDS bank exactly once.
-__device__ __forceinline__ int vt_chunk(int d, int chunk) { return chunk ^ ((d + (d >> 3)) & 7); }
-
+// Physical chunk for V rows: the 4 rows x 64 bytes a half-wavefront
+// transpose-reads at once land in distinct bank groups.
 template <int D>
-struct Tiles {
-    static constexpr int kKStride = D + 8;            // halves per K row in LDS (16-byte pad)
-    static constexpr int kKTile = kBN * kKStride;     // halves
-    static constexpr int kVTile = D * kBN;            // halves
-    static constexpr int kKUnits = kBN * D / 8;       // 16-byte K chunks per tile
-    static constexpr int kKPerThread = kKUnits / kThreads;
-    static constexpr int kDGroups = D / 8;
-    static constexpr int kVUnits = (kBN / 4) * kDGroups;  // (4 keys x 8 d) blocks per tile
-    static constexpr int kVPerThread = (kVUnits + kThreads - 1) / kThreads;
-    static_assert(kKUnits % kThreads == 0, "K tile must split evenly");
+__device__ __forceinline__ int v_chunk(int row, int c)
+{
+    return D == 128 ? (c ^ ((row & 3) << 2)) : (c ^ (((row >> 1) & 1) << 2));
+}
+
+// Byte offsets, relative to the first key row of a tile, of the 16-byte
+// chunks this lane copies with each of its direct loads (same for K and V
+// up to the swizzle).  Rows of a tile are < 64 apart, so they fit 32 bits.
+template <int D>
+struct LoadOffsets {
+    uint32_t k[Geo<D>::kLoadsPerWave], v[Geo<D>::kLoadsPerWave];
+    int row[Geo<D>::kLoadsPerWave];
 };
 
 template <int D>
-struct Prefetch {
-    u32x4 k[Tiles<D>::kKPerThread];
-    u32x4 v[Tiles<D>::kVPerThread][4];
-};
-
-// Global -> registers for the K/V tile starting at key k0.  Rows at or past
-// L are zero-filled so masked keys carry finite values.
-template <int D>
-__device__ __forceinline__ void load_tile(Prefetch<D> &pf, const _Float16 *kbase,
-                                          const _Float16 *vbase, int64_t kv_row, int k0, int L)
+__device__ __forceinline__ void init_load_offsets(LoadOffsets<D> &lo, int64_t kv_row)
 {
-    using T = Tiles<D>;
-    const int tid = threadIdx.x;
+    using G = Geo<D>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int r = 0; r < T::kKPerThread; ++r) {
-        int u = tid + r * kThreads;
-        int row = u / T::kDGroups, ch = u % T::kDGroups;
-        int key = k0 + row;
-        u32x4 val = {0, 0, 0, 0};
-        if (key < L) val = *(const u32x4 *)(kbase + (int64_t)key * kv_row + ch * 8);
-        pf.k[r] = val;
-    }
-#pragma unroll
-    for (int r = 0; r < T::kVPerThread; ++r) {
-        int u = tid + r * kThreads;
-        // u = kg_hi * (4 * kDGroups) + dg * 4 + kg_lo, kg = 4 * kg_hi + kg_lo
-        int kg = 4 * (u / (4 * T::kDGroups)) + (u & 3);
-        int dg = (u >> 2) % T::kDGroups;
-        bool active = u < T::kVUnits;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int key = k0 + 4 * kg + j;
-            u32x4 val = {0, 0, 0, 0};
-            if (active && key < L) val = *(const u32x4 *)(vbase + (int64_t)key * kv_row + dg * 8);
-            pf.v[r][j] = val;
-        }
+    for (int n = 0; n < G::kLoadsPerWave; ++n) {
+        const int blk = G::kLoadsPerWave * wave + n;
+        const int row = G::kRowsPerLoad * blk + lane / G::kChunks;
+        const int pc = lane % G::kChunks;
+        lo.row[n] = row;
+        lo.k[n] = (uint32_t)(2 * (row * kv_row + 8 * k_chunk<D>(row, pc)));
+        lo.v[n] = (uint32_t)(2 * (row * kv_row + 8 * v_chunk<D>(row, pc)));
     }
 }
 
-// Registers -> LDS: K row-major (padded), V transposed into V^T[d][position].
+// Issue this wave's share of the direct HBM -> LDS loads of the K and V tiles
+// that start at key k0.  A tile reaching past L loads row L-1 in place of the
+// missing rows (finite data that the mask hides).
 template <int D>
-__device__ __forceinline__ void store_tile(const Prefetch<D> &pf, _Float16 *klds, _Float16 *vlds)
+__device__ __forceinline__ void issue_tile_loads(const LoadOffsets<D> &lo, const _Float16 *kbase,
+                                                 const _Float16 *vbase, int64_t kv_row, int k0,
+                                                 int L, _Float16 *klds, _Float16 *vlds)
 {
-    using T = Tiles<D>;
-    const int tid = threadIdx.x;
+    using G = Geo<D>;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const char *kt = (const char *)(kbase + (int64_t)k0 * kv_row);
+    const char *vt = (const char *)(vbase + (int64_t)k0 * kv_row);
+    const bool full = k0 + kBN <= L;
 #pragma unroll
-    for (int r = 0; r < T::kKPerThread; ++r) {
-        int u = tid + r * kThreads;
-        int row = u / T::kDGroups, ch = u % T::kDGroups;
-        *(u32x4 *)(klds + row * T::kKStride + ch * 8) = pf.k[r];
-    }
-#pragma unroll
-    for (int r = 0; r < T::kVPerThread; ++r) {
-        int u = tid + r * kThreads;
-        if (u >= T::kVUnits) continue;
-        int kg = 4 * (u / (4 * T::kDGroups)) + (u & 3);
-        int dg = (u >> 2) % T::kDGroups;
-        int pos = vt_position(4 * kg);  // the 4 keys stay contiguous
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            int w = e >> 1;
-            uint32_t a0 = pf.v[r][0][w], a1 = pf.v[r][1][w], a2 = pf.v[r][2][w], a3 = pf.v[r][3][w];
-            u32x2 out;
-            if (e & 1) {
-                out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-            } else {
-                out[0] = (a0 & 0xffffu) | (a1 << 16);
-                out[1] = (a2 & 0xffffu) | (a3 << 16);
+    for (int n = 0; n < G::kLoadsPerWave; ++n) {
+        const int blk = G::kLoadsPerWave * wave + n;
+        uint32_t ko = lo.k[n], vo = lo.v[n];
+        if (!full) {
+            const int over = k0 + lo.row[n] - (L - 1);  // rows past the end re-read row L-1
+            if (over > 0) {
+                ko -= (uint32_t)(2 * over * kv_row);
+                vo -= (uint32_t)(2 * over * kv_row);
             }
-            int d = 8 * dg + e;
-            int off = d * kBN + 8 * vt_chunk(d, pos >> 3) + (pos & 7);
-            *(u32x2 *)(vlds + off) = out;
         }
+        __builtin_amdgcn_global_load_lds((const void *)(kt + (uint64_t)ko),
+                                         (LDS_AS void *)(klds + 512 * blk), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(vt + (uint64_t)vo),
+                                         (LDS_AS void *)(vlds + 512 * blk), 16, 0, 0);
     }
 }
 
-// Work item -> (b, kv head, group member, q block).  Items are ordered so
-// that the query heads sharing one K/V head, and all q blocks of each, are
-// consecutive.
+__device__ __forceinline__ half8 lds_read16(const _Float16 *p) { return *(const half8 *)p; }
+
+__device__ __forceinline__ half4 lds_read_tr(const _Float16 *p)
+{
+    short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)(p));
+    return __builtin_bit_cast(half4, v);
+}
+
+// Work item -> position in the (b, kv head, group member, q block) order.
 __device__ __forceinline__ int xcd_item(int block, int n)
 {
     int x = block % kXcds, slot = block / kXcds;
@@ -204,173 +197,235 @@ __device__ __forceinline__ int xcd_item(int block, int n)
 }
 
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(2, 2))) void
-fa_fwd_kernel(const Args a)
-{
-    using T = Tiles<D>;
-    constexpr int kSteps = D / 16;   // k-steps of S^T = K.Q^T
-    constexpr int kDBlocks = D / 32; // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) _Float16 klds[2][T::kKTile];
-    __shared__ __attribute__((aligned(16))) _Float16 vlds[2][T::kVTile];
+struct Kernel {
+    using G = Geo<D>;
+    static constexpr int kSteps = D / 16;    // k-steps of S^T = K.Q^T
+    static constexpr int kDBlocks = D / 32;  // 32-row blocks of O^T
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 31, half = lane >> 5;
+    // per-lane state of one wavefront
+    struct State {
+        half8 qf[kSteps];
+        floatx16 oacc[kDBlocks];
+        float m;    // reference row maximum (raw score units)
+        float l;    // running row sum, this lane's keys
+        int k_addr[kSteps];   // LDS half offsets of this lane's K reads, per k-step
+        int v_addr[kDBlocks]; // LDS half offsets of this lane's V transpose reads, per d block
+    };
 
-    // ---- work item
-    const int item = xcd_item(blockIdx.x, a.n_items);
-    int rest = item / a.n_qblocks;
-    int qb = item % a.n_qblocks;
-    if (CAUSAL) qb = a.n_qblocks - 1 - qb;  // heaviest blocks first
-    const int g = rest % a.groups;
-    rest /= a.groups;
-    const int hk = rest % a.Hkv;
-    const int b = rest / a.Hkv;
-    const int h = hk * a.groups + g;
-    const int L = a.L;
-    const int q0 = qb * kBM;
-
-    const int64_t q_row = (int64_t)a.H * D, kv_row = (int64_t)a.Hkv * D;
-    const _Float16 *qbase = a.q + (int64_t)b * L * q_row + (int64_t)h * D;
-    const _Float16 *kbase = a.k + (int64_t)b * L * kv_row + (int64_t)hk * D;
-    const _Float16 *vbase = a.v + (int64_t)b * L * kv_row + (int64_t)hk * D;
-
-    // ---- Q block -> B-operand fragments (lane: query q0 + 32*wave + col)
-    const int wq0 = q0 + 32 * wave;
-    const int qi = wq0 + col;
-    half8 qf[kSteps];
+    __device__ __forceinline__ static void tile(State &st, const _Float16 *kl, const _Float16 *vl,
+                                                int k0, int L, int wq0, int qi, float c)
+    {
+        const int lane = threadIdx.x & 63;
+        const int half = lane >> 5;
+        // S^T = K . Q^T for the 64 keys of the tile, as two 32-key blocks
+        floatx16 sacc[2] = {floatx16{}, floatx16{}};
+        half8 ka[2][2];
+        ka[0][0] = lds_read16(kl + st.k_addr[0]);
+        ka[0][1] = lds_read16(kl + st.k_addr[0] + 32 * D);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        half8 val = {};
-        if (qi < L) val = *(const half8 *)(qbase + (int64_t)qi * q_row + 16 * s + 8 * half);
-        qf[s] = val;
-    }
-
-    floatx16 oacc[kDBlocks];
-#pragma unroll
-    for (int i = 0; i < kDBlocks; ++i) oacc[i] = floatx16{};
-    float m = -__builtin_huge_valf();  // running row max (raw score units)
-    float l = 0.0f;                    // running row sum (this lane's keys)
-
-    const int kv_end = CAUSAL ? (q0 + kBM < L ? q0 + kBM : L) : L;
-    const int n_tiles = (kv_end + kBN - 1) / kBN;
-    const float c = a.scale_log2;
-
-    Prefetch<D> pf;
-    load_tile<D>(pf, kbase, vbase, kv_row, 0, L);
-    store_tile<D>(pf, klds[0], vlds[0]);
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int k0 = t * kBN;
-        const bool more = t + 1 < n_tiles;
-        if (more) load_tile<D>(pf, kbase, vbase, kv_row, k0 + kBN, L);
-        __syncthreads();
-        const _Float16 *kl = klds[t & 1];
-        const _Float16 *vl = vlds[t & 1];
-
-        // A wavefront whose 32 queries all precede this tile has nothing to do.
-        const bool active = !CAUSAL || k0 <= wq0 + 31;
-        if (active) {
-            // S^T = K . Q^T for the 64 keys of the tile, as two 32-key blocks
-            floatx16 sacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                floatx16 acc = {};
-#pragma unroll
-                for (int s = 0; s < kSteps; ++s) {
-                    half8 ka = *(const half8 *)(kl + (32 * kb + col) * T::kKStride + 16 * s + 8 * half);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[s], acc, 0, 0, 0);
-                }
-                sacc[kb] = acc;
+        for (int s = 0; s < kSteps; ++s) {
+            if (s + 1 < kSteps) {  // next k-step's fragments in flight during this one
+                ka[(s + 1) & 1][0] = lds_read16(kl + st.k_addr[s + 1]);
+                ka[(s + 1) & 1][1] = lds_read16(kl + st.k_addr[s + 1] + 32 * D);
             }
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s & 1][0], st.qf[s], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s & 1][1], st.qf[s], sacc[1], 0, 0, 0);
+        }
 
-            // mask: keys past the sequence end, and keys after the query (causal)
-            const bool need_mask = (k0 + kBN > L) || (CAUSAL && k0 + kBN - 1 > wq0);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-                        bool hide = key >= L || (CAUSAL && key > qi);
-                        if (hide) sacc[kb][r] = -__builtin_huge_valf();
-                    }
-            }
-
-            // online softmax (exp via exp2 with scale*log2(e) folded in)
-            float mx = sacc[0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = pair_max(mx);
-            const float m_new = fmaxf(m, mx);
-            const float mc = m_new * c;
-            const float sf = exp2_fast(m * c - mc);
-            float rs = 0.0f;
+        // mask: keys past the sequence end, and keys after the query (causal)
+        const bool need_mask = (k0 + kBN > L) || (CAUSAL && k0 + kBN - 1 > wq0);
+        if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float p = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -mc));
-                    sacc[kb][r] = p;
-                    rs += p;
+                    const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+                    const bool hide = key >= L || (CAUSAL && key > qi);
+                    if (hide) sacc[kb][r] = -__builtin_huge_valf();
                 }
-            l = l * sf + rs;
-            m = m_new;
+        }
+
+        // row maximum of the tile, both lane halves
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = pair_max(mx);
+
+        // lazy rescale: raise the reference maximum only when some row's
+        // maximum outgrew it by more than 2^kRescaleLog2
+        const bool grow = (mx - st.m) * c > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = fmaxf(st.m, mx);
+            const float sf = exp2_fast((st.m - m_new) * c);
+            st.l *= sf;
 #pragma unroll
             for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[i][r] *= sf;
-
-            // P^T k-steps (16 keys each) as fp16 B operands, round-to-nearest-even
-            half8 pfrag[4];
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs) {
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    float2v f2 = {sacc[cs >> 1][8 * (cs & 1) + e], sacc[cs >> 1][8 * (cs & 1) + e + 1]};
-                    half2v h2 = __builtin_convertvector(f2, half2v);
-                    pfrag[cs][e] = h2[0];
-                    pfrag[cs][e + 1] = h2[1];
-                }
-            }
-
-            // O^T += V^T . P^T
-#pragma unroll
-            for (int i = 0; i < kDBlocks; ++i) {
-                const int d = 32 * i + col;
-#pragma unroll
-                for (int cs = 0; cs < 4; ++cs) {
-                    half8 va = *(const half8 *)(vl + d * kBN + 8 * vt_chunk(d, 2 * cs + half));
-                    oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pfrag[cs], oacc[i], 0, 0, 0);
-                }
-            }
+                for (int r = 0; r < 16; ++r) st.oacc[i][r] *= sf;
+            st.m = m_new;
         }
+        const float mc = st.m * c;
 
-        if (more) store_tile<D>(pf, klds[(t + 1) & 1], vlds[(t + 1) & 1]);
-    }
+        // P = exp2(S*c - m*c); row sum in four partial sums
+        float rs[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -mc));
+                sacc[kb][r] = p;
+                if (kb == 0 && r < 4)
+                    rs[r] = p;
+                else
+                    rs[r & 3] += p;
+            }
+        st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
-    // ---- finalise: O = acc / l (guarded as on the page), LSE = scale*m + ln l
-    const float lt = pair_sum(l);
-    const float inv = 1.0f / (lt > 1e-6f ? lt : 1.0f);
-    if (qi < L) {
-        _Float16 *orow = a.o + (int64_t)b * L * q_row + (int64_t)qi * q_row + (int64_t)h * D;
+        // P^T k-steps (16 keys each) as fp16 B operands, round-to-nearest-even
+        half8 pf[4];
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float2v f2 = {sacc[cs >> 1][8 * (cs & 1) + e], sacc[cs >> 1][8 * (cs & 1) + e + 1]};
+                const half2v h2 = __builtin_convertvector(f2, half2v);
+                pf[cs][e] = h2[0];
+                pf[cs][e + 1] = h2[1];
+            }
+
+        // O^T += V^T . P^T ; the A operand of k-step cs is two transpose reads:
+        // keys 16cs + 4h + 0..3 and 16cs + 8 + 4h + 0..3 for lane half h
 #pragma unroll
         for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                float2v lo = {oacc[i][4 * rb + 0] * inv, oacc[i][4 * rb + 1] * inv};
-                float2v hi = {oacc[i][4 * rb + 2] * inv, oacc[i][4 * rb + 3] * inv};
-                half2v hl = __builtin_convertvector(lo, half2v);
-                half2v hh = __builtin_convertvector(hi, half2v);
-                half4 out = {hl[0], hl[1], hh[0], hh[1]};
-                *(half4 *)(orow + 32 * i + 8 * rb + 4 * half) = out;
+            for (int cs = 0; cs < 4; ++cs) {
+                const half4 lo = lds_read_tr(vl + st.v_addr[i] + 16 * cs * D);
+                const half4 hi = lds_read_tr(vl + st.v_addr[i] + (16 * cs + 8) * D);
+                const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                st.oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[cs], st.oacc[i], 0, 0, 0);
             }
-        if (a.lse && half == 0)
-            a.lse[((int64_t)b * a.H + h) * L + qi] = m * a.scale + __logf(lt);
     }
+
+    __device__ static void run(const Args &a)
+    {
+        __shared__ __attribute__((aligned(16))) _Float16 klds[2][G::kTile];
+        __shared__ __attribute__((aligned(16))) _Float16 vlds[2][G::kTile];
+
+        const int tid = threadIdx.x;
+        const int lane = tid & 63, wave = tid >> 6;
+        const int col = lane & 31, half = lane >> 5;
+
+        // ---- work item
+        const int item = xcd_item(blockIdx.x, a.n_items);
+        int rest = item / a.n_qblocks;
+        int qb = item % a.n_qblocks;
+        if (CAUSAL) qb = a.n_qblocks - 1 - qb;  // heaviest blocks first
+        const int g = rest % a.groups;
+        rest /= a.groups;
+        const int hk = rest % a.Hkv;
+        const int b = rest / a.Hkv;
+        const int h = hk * a.groups + g;
+        const int L = a.L;
+        const int q0 = qb * kBM;
+
+        const int64_t q_row = (int64_t)a.H * D, kv_row = (int64_t)a.Hkv * D;
+        const _Float16 *qbase = a.q + (int64_t)b * L * q_row + (int64_t)h * D;
+        const _Float16 *kbase = a.k + (int64_t)b * L * kv_row + (int64_t)hk * D;
+        const _Float16 *vbase = a.v + (int64_t)b * L * kv_row + (int64_t)hk * D;
+
+        const int kv_end = CAUSAL ? (q0 + kBM < L ? q0 + kBM : L) : L;
+        const int n_tiles = (kv_end + kBN - 1) / kBN;
+
+        // first tile in flight while Q is fetched
+        LoadOffsets<D> lo;
+        init_load_offsets<D>(lo, kv_row);
+        issue_tile_loads<D>(lo, kbase, vbase, kv_row, 0, L, klds[0], vlds[0]);
+
+        State st;
+        const int wq0 = q0 + 32 * wave;
+        const int qi = wq0 + col;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            half8 val = {};
+            if (qi < L) val = *(const half8 *)(qbase + (int64_t)qi * q_row + 16 * s + 8 * half);
+            st.qf[s] = val;
+        }
+#pragma unroll
+        for (int i = 0; i < kDBlocks; ++i) st.oacc[i] = floatx16{};
+        st.m = -__builtin_huge_valf();
+        st.l = 0.0f;
+        // K: row = 32*kb + col, logical chunk 2s + half
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) st.k_addr[s] = col * D + 8 * k_chunk<D>(col, 2 * s + half);
+        // V transpose read: 16-lane group gg = lane/16 (d half gg%2, key half gg/2),
+        // j = lane%16 -> row 4*(gg/2) + j/4 (+ 16*cs [+ 8]), d = 32*i + 16*(gg%2) + 4*(j%4)
+        {
+            const int gg = lane >> 4, j = lane & 15;
+            const int row = 4 * (gg >> 1) + (j >> 2);
+#pragma unroll
+            for (int i = 0; i < kDBlocks; ++i) {
+                const int d = 32 * i + 16 * (gg & 1) + 4 * (j & 3);
+                st.v_addr[i] = row * D + 8 * v_chunk<D>(row, d >> 3) + (d & 7);
+            }
+        }
+
+        const float c = a.scale_log2;
+        for (int t = 0; t < n_tiles; t += 2) {
+            step<0>(st, lo, kbase, vbase, kv_row, t, n_tiles, L, wq0, qi, c, klds, vlds);
+            if (t + 1 < n_tiles)
+                step<1>(st, lo, kbase, vbase, kv_row, t + 1, n_tiles, L, wq0, qi, c, klds, vlds);
+        }
+
+        // ---- finalise: O = acc / l (guarded as on the page), LSE = scale*m + ln l
+        const float lt = pair_sum(st.l);
+        const float inv = 1.0f / (lt > 1e-6f ? lt : 1.0f);
+        if (qi < L) {
+            _Float16 *orow = a.o + (int64_t)b * L * q_row + (int64_t)qi * q_row + (int64_t)h * D;
+#pragma unroll
+            for (int i = 0; i < kDBlocks; ++i)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const float2v lo = {st.oacc[i][4 * rb + 0] * inv, st.oacc[i][4 * rb + 1] * inv};
+                    const float2v hi = {st.oacc[i][4 * rb + 2] * inv, st.oacc[i][4 * rb + 3] * inv};
+                    const half2v hl = __builtin_convertvector(lo, half2v);
+                    const half2v hh = __builtin_convertvector(hi, half2v);
+                    const half4 out = {hl[0], hl[1], hh[0], hh[1]};
+                    *(half4 *)(orow + 32 * i + 8 * rb + 4 * half) = out;
+                }
+            if (a.lse && half == 0)
+                a.lse[((int64_t)b * a.H + h) * L + qi] = st.m * a.scale + __logf(lt);
+        }
+    }
+
+    // One K/V tile: wait for its loads, barrier, start the next tile's loads
+    // into the other buffer, compute.  BUF is the buffer tile t lives in.
+    template <int BUF>
+    __device__ __forceinline__ static void step(State &st, const LoadOffsets<D> &lo,
+                                                const _Float16 *kbase,
+                                                const _Float16 *vbase, int64_t kv_row, int t,
+                                                int n_tiles, int L, int wq0, int qi, float c,
+                                                _Float16 (*klds)[G::kTile],
+                                                _Float16 (*vlds)[G::kTile])
+    {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t have landed
+        __syncthreads();                // ... and every wave's; tile t-1 fully consumed
+        if (t + 1 < n_tiles)
+            issue_tile_loads<D>(lo, kbase, vbase, kv_row, (t + 1) * kBN, L, klds[BUF ^ 1],
+                                vlds[BUF ^ 1]);
+        const int k0 = t * kBN;
+        // a wavefront whose 32 queries all precede this tile has nothing to do
+        if (!CAUSAL || k0 <= wq0 + 31) tile(st, klds[BUF], vlds[BUF], k0, L, wq0, qi, c);
+    }
+};
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(2, 2))) void
+fa_fwd_kernel(const Args a)
+{
+    Kernel<D, CAUSAL>::run(a);
 }
 
 template <int D, bool CAUSAL>
@@ -398,6 +453,8 @@ int launch_forward(const Problem &p, hipStream_t stream)
     a.n_qblocks = (p.L + kBM - 1) / kBM;
     int64_t items = (int64_t)p.B * p.H * a.n_qblocks;
     if (items > 0x7fffffff) return FA_ERR_SHAPE;
+    // per-lane tile offsets are 32-bit: a tile of kBN K/V rows must span < 2 GiB
+    if ((int64_t)p.Hkv * p.D * 2 * kBN > 0x7fffffff) return FA_ERR_SHAPE;
     a.n_items = (int)items;
     a.scale = p.scale;
     a.scale_log2 = p.scale * 1.4426950408889634f;
