@@ -62,7 +62,7 @@ def test_tiny_workload(seed, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("L", [1, 3, 63, 64, 65, 100, 127, 128, 129, 200, 1000])
+@pytest.mark.parametrize("L", [1, 3, 63, 64, 65, 100, 127, 128, 129, 200, 255, 256, 257, 511, 1000])
 def test_ragged_lengths(L, D, causal):
     full_case(1, L, 2, 1, D, causal, seed=L)
 

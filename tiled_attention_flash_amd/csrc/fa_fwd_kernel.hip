@@ -11,8 +11,11 @@
 //
 // Mapping onto CDNA4
 // ------------------
-// * Workgroup = 4 wavefronts (256 lanes) owning one block of BM = 128 query
-//   rows of one (batch, query head); each wavefront owns 32 whole query rows.
+// * Workgroup = W wavefronts owning one block of BM = 32*W query rows of one
+//   (batch, query head); each wavefront owns 32 whole query rows.  W = 8 for
+//   the full (non-causal) pass -- each K/V tile brought into LDS then serves
+//   256 queries -- and W = 4 under the causal mask, where the smaller block
+//   keeps the wavefronts of a workgroup evenly loaded along the diagonal.
 // * Both products are computed transposed, on v_mfma_f32_32x32x16_f16:
 //     S^T[key][query]  = K . Q^T     (A = K rows from LDS, B = Q in VGPRs)
 //     O^T[d][query]   += V^T . P^T   (A = V^T from LDS,   B = P in VGPRs)
@@ -28,16 +31,17 @@
 //   16-lane group column i of the 4x16 block its group points at) builds the
 //   V^T operand in exactly that key order, so P never leaves registers.
 // * K/V tiles of BN = 64 keys travel HBM -> LDS with global_load_lds_dwordx4
-//   (16 bytes per lane, no staging registers), double-buffered, one
-//   workgroup barrier per tile.  The source address of each lane is chosen so
-//   that rows land with a 16-byte-chunk XOR swizzle that makes the K reads
+//   (16 bytes per lane, no staging registers), double-buffered with one
+//   workgroup barrier per tile; the next tile's loads fly while the current
+//   one is computed.  The source address of each lane is chosen so that rows
+//   land with a 16-byte-chunk XOR swizzle that makes the K reads
 //   (ds_read_b128, 16 rows per LDS cycle) and the V transpose reads (4 rows x
-//   64 bytes per half-wavefront) free of bank conflicts.  Rows past the end of
-//   the sequence load row L-1 instead (finite data that the mask hides).
+//   64 bytes per half-wavefront) free of bank conflicts.  Rows past the end
+//   of the sequence load row L-1 instead (finite data that the mask hides).
 // * Online softmax with a lazy rescale: the reference maximum of a row is
 //   raised (and O, l rescaled) only when some row of the wavefront sees its
 //   maximum grow by more than 2^8 in the exp2 domain; otherwise the stale
-//   maximum keeps every probability <= 256 (exact in fp16's range) and the
+//   maximum keeps every probability <= 256 (well inside fp16's range) and the
 //   final O / l and LSE are unchanged.
 // * Causal: tiles past the block's last query are never visited; the mask
 //   code runs only on tiles that straddle a wavefront's diagonal (or hold the
@@ -63,10 +67,7 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per work item
-constexpr int kBN = 64;           // keys per K/V tile
+constexpr int kBN = 64;               // keys per K/V tile
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
 
@@ -97,15 +98,16 @@ __device__ __forceinline__ float pair_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Tile geometry.  A tile row is D halves = D/8 chunks of 16 bytes.
-template <int D>
+// Tile geometry for head dim D and W wavefronts.  A tile row is D halves =
+// D/8 chunks of 16 bytes; one wave-wide direct load fills 1 KiB of LDS.
+template <int D, int W>
 struct Geo {
-    static constexpr int kChunks = D / 8;               // 16-byte chunks per row
-    static constexpr int kRowsPerLoad = 64 / kChunks;   // rows one wave load instruction fills
+    static constexpr int kChunks = D / 8;              // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kChunks;  // rows one wave load instruction fills
     static constexpr int kLoadsPerTile = kBN / kRowsPerLoad;
-    static constexpr int kLoadsPerWave = kLoadsPerTile / kWaves;
-    static constexpr int kTile = kBN * D;               // halves per K (or V) tile
-    static_assert(kLoadsPerTile % kWaves == 0, "tile loads must split over the waves");
+    static constexpr int kLoadsPerWave = kLoadsPerTile / W;
+    static constexpr int kTile = kBN * D;  // halves per K (or V) tile
+    static_assert(kLoadsPerTile % W == 0, "tile loads must split over the waves");
 };
 
 // Physical 16-byte chunk of logical chunk `c` of K row `row`: 16 consecutive
@@ -124,40 +126,61 @@ __device__ __forceinline__ int v_chunk(int row, int c)
     return D == 128 ? (c ^ ((row & 3) << 2)) : (c ^ (((row >> 1) & 1) << 2));
 }
 
+// Tile row that this lane's n-th direct load fills.
+template <int D, int W>
+__device__ __forceinline__ int load_row(int n)
+{
+    using G = Geo<D, W>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return G::kRowsPerLoad * (G::kLoadsPerWave * wave + n) + lane / G::kChunks;
+}
+
 // Byte offsets, relative to the first key row of a tile, of the 16-byte
-// chunks this lane copies with each of its direct loads (same for K and V
-// up to the swizzle).  Rows of a tile are < 64 apart, so they fit 32 bits.
-template <int D>
+// chunks this lane copies with each of its direct loads.  Rows of a tile are
+// < 64 apart, so the offsets fit 32 bits (the host checks Hkv*D).
+template <int D, int W>
 struct LoadOffsets {
-    uint32_t k[Geo<D>::kLoadsPerWave], v[Geo<D>::kLoadsPerWave];
-    int row[Geo<D>::kLoadsPerWave];
+    uint32_t k[Geo<D, W>::kLoadsPerWave], v[Geo<D, W>::kLoadsPerWave];
 };
 
-template <int D>
-__device__ __forceinline__ void init_load_offsets(LoadOffsets<D> &lo, int64_t kv_row)
+template <int D, int W>
+__device__ __forceinline__ void init_load_offsets(LoadOffsets<D, W> &lo, int64_t kv_row)
 {
-    using G = Geo<D>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    using G = Geo<D, W>;
+    const int pc = (threadIdx.x & 63) % G::kChunks;
 #pragma unroll
     for (int n = 0; n < G::kLoadsPerWave; ++n) {
-        const int blk = G::kLoadsPerWave * wave + n;
-        const int row = G::kRowsPerLoad * blk + lane / G::kChunks;
-        const int pc = lane % G::kChunks;
-        lo.row[n] = row;
+        const int row = load_row<D, W>(n);
         lo.k[n] = (uint32_t)(2 * (row * kv_row + 8 * k_chunk<D>(row, pc)));
         lo.v[n] = (uint32_t)(2 * (row * kv_row + 8 * v_chunk<D>(row, pc)));
     }
 }
 
-// Issue this wave's share of the direct HBM -> LDS loads of the K and V tiles
-// that start at key k0.  A tile reaching past L loads row L-1 in place of the
-// missing rows (finite data that the mask hides).
-template <int D>
-__device__ __forceinline__ void issue_tile_loads(const LoadOffsets<D> &lo, const _Float16 *kbase,
-                                                 const _Float16 *vbase, int64_t kv_row, int k0,
-                                                 int L, _Float16 *klds, _Float16 *vlds)
+// One 16-byte-per-lane direct HBM -> LDS load: lane i's 16 bytes from
+// base + off land at lds + 16*i.  Written as inline assembly so that the
+// compiler does not see the LDS tile buffers as written by an in-flight load
+// and stall every later LDS read until all loads complete (it cannot tell
+// the two buffers apart); the kernel itself waits for a tile's loads before
+// the barrier that hands the tile to the workgroup.
+__device__ __forceinline__ void dma16(const char *base, uint32_t off, _Float16 *lds)
 {
-    using G = Geo<D>;
+    const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void *)lds;
+    __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :
+                     : "v"(off), "s"(base), "{m0}"(m0)
+                     : "memory");
+}
+
+// Issue this wave's share of the direct loads of the K and V tiles that start
+// at key k0.  A tile reaching past L loads row L-1 in place of the missing
+// rows (finite data that the mask hides).
+template <int D, int W>
+__device__ __forceinline__ void issue_tile_loads(const LoadOffsets<D, W> &lo,
+                                                 const _Float16 *kbase, const _Float16 *vbase,
+                                                 int64_t kv_row, int k0, int L, _Float16 *klds,
+                                                 _Float16 *vlds)
+{
+    using G = Geo<D, W>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const char *kt = (const char *)(kbase + (int64_t)k0 * kv_row);
     const char *vt = (const char *)(vbase + (int64_t)k0 * kv_row);
@@ -167,16 +190,14 @@ __device__ __forceinline__ void issue_tile_loads(const LoadOffsets<D> &lo, const
         const int blk = G::kLoadsPerWave * wave + n;
         uint32_t ko = lo.k[n], vo = lo.v[n];
         if (!full) {
-            const int over = k0 + lo.row[n] - (L - 1);  // rows past the end re-read row L-1
+            const int over = k0 + load_row<D, W>(n) - (L - 1);  // rows past the end re-read row L-1
             if (over > 0) {
                 ko -= (uint32_t)(2 * over * kv_row);
                 vo -= (uint32_t)(2 * over * kv_row);
             }
         }
-        __builtin_amdgcn_global_load_lds((const void *)(kt + (uint64_t)ko),
-                                         (LDS_AS void *)(klds + 512 * blk), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(vt + (uint64_t)vo),
-                                         (LDS_AS void *)(vlds + 512 * blk), 16, 0, 0);
+        dma16(kt, ko, klds + 512 * blk);
+        dma16(vt, vo, vlds + 512 * blk);
     }
 }
 
@@ -196,9 +217,11 @@ __device__ __forceinline__ int xcd_item(int block, int n)
     return x * per + (x < extra ? x : extra) + slot;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int W>
 struct Kernel {
-    using G = Geo<D>;
+    using G = Geo<D, W>;
+    static constexpr int kThreads = 64 * W;
+    static constexpr int kBM = 32 * W;       // query rows per work item
     static constexpr int kSteps = D / 16;    // k-steps of S^T = K.Q^T
     static constexpr int kDBlocks = D / 32;  // 32-row blocks of O^T
 
@@ -206,43 +229,53 @@ struct Kernel {
     struct State {
         half8 qf[kSteps];
         floatx16 oacc[kDBlocks];
-        float m;    // reference row maximum (raw score units)
-        float l;    // running row sum, this lane's keys
-        int k_addr[kSteps];   // LDS half offsets of this lane's K reads, per k-step
-        int v_addr[kDBlocks]; // LDS half offsets of this lane's V transpose reads, per d block
+        float m;     // reference row maximum (raw score units)
+        float l;     // running row sum, this lane's keys
+        int k_base;  // LDS half offset of this lane's K read at k-step 0
+        int v_base;  // LDS half offset of this lane's V transpose read at d block 0
     };
+
+    // The swizzles are XORs on the 16-byte chunk index, and the chunk index
+    // of k-step s (d block i) differs from that of step 0 (block 0) only in
+    // bits the XOR touches, so each read address is one XOR from the base.
+    __device__ __forceinline__ static int k_offset(const State &st, int s) { return st.k_base ^ (16 * s); }
+    __device__ __forceinline__ static int v_offset(const State &st, int i) { return st.v_base ^ (32 * i); }
 
     __device__ __forceinline__ static void tile(State &st, const _Float16 *kl, const _Float16 *vl,
                                                 int k0, int L, int wq0, int qi, float c)
     {
-        const int lane = threadIdx.x & 63;
-        const int half = lane >> 5;
-        // S^T = K . Q^T for the 64 keys of the tile, as two 32-key blocks
+        const int half = (threadIdx.x & 63) >> 5;
+
+        // S^T = K . Q^T for the 64 keys of the tile, as two 32-key blocks;
+        // the next k-step's K fragments are read during the current one
         floatx16 sacc[2] = {floatx16{}, floatx16{}};
         half8 ka[2][2];
-        ka[0][0] = lds_read16(kl + st.k_addr[0]);
-        ka[0][1] = lds_read16(kl + st.k_addr[0] + 32 * D);
+        ka[0][0] = lds_read16(kl + k_offset(st, 0));
+        ka[0][1] = lds_read16(kl + k_offset(st, 0) + 32 * D);
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-            if (s + 1 < kSteps) {  // next k-step's fragments in flight during this one
-                ka[(s + 1) & 1][0] = lds_read16(kl + st.k_addr[s + 1]);
-                ka[(s + 1) & 1][1] = lds_read16(kl + st.k_addr[s + 1] + 32 * D);
+            if (s + 1 < kSteps) {
+                ka[(s + 1) & 1][0] = lds_read16(kl + k_offset(st, s + 1));
+                ka[(s + 1) & 1][1] = lds_read16(kl + k_offset(st, s + 1) + 32 * D);
             }
             sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s & 1][0], st.qf[s], sacc[0], 0, 0, 0);
             sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s & 1][1], st.qf[s], sacc[1], 0, 0, 0);
         }
 
-        // mask: keys past the sequence end, and keys after the query (causal)
-        const bool need_mask = (k0 + kBN > L) || (CAUSAL && k0 + kBN - 1 > wq0);
-        if (need_mask) {
+        // mask: keys past the sequence end, and keys after the query (causal).
+        // Register r of block kb holds key k0 + 4*half + 32kb + 8(r/4) + r%4,
+        // so one per-lane bound decides every element.
+        if ((k0 + kBN > L) || (CAUSAL && k0 + kBN - 1 > wq0)) {
+            int bound = L - k0 - 4 * half;  // hide offsets >= bound
+            if (CAUSAL) {
+                const int cb = qi - k0 - 4 * half + 1;
+                bound = cb < bound ? cb : bound;
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const bool hide = key >= L || (CAUSAL && key > qi);
-                    if (hide) sacc[kb][r] = -__builtin_huge_valf();
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) >= bound) sacc[kb][r] = -__builtin_huge_valf();
         }
 
         // row maximum of the tile, both lane halves
@@ -268,44 +301,45 @@ struct Kernel {
         }
         const float mc = st.m * c;
 
-        // P = exp2(S*c - m*c); row sum in four partial sums
-        float rs[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -mc));
-                sacc[kb][r] = p;
-                if (kb == 0 && r < 4)
-                    rs[r] = p;
-                else
-                    rs[r & 3] += p;
-            }
-        st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-
-        // P^T k-steps (16 keys each) as fp16 B operands, round-to-nearest-even
+        // P = exp2(S*c - m*c) as fp16 B operands (round-to-nearest-even), one
+        // per 16-key k-step, and the tile's row sum in four partial sums
+        // (partial sum a = 2(cs&1) + e/4 is first written at cs < 2, e in {0,4})
         half8 pf[4];
+        float rs[4];
 #pragma unroll
         for (int cs = 0; cs < 4; ++cs)
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float2v f2 = {sacc[cs >> 1][8 * (cs & 1) + e], sacc[cs >> 1][8 * (cs & 1) + e + 1]};
+                const int kb = cs >> 1, r = 8 * (cs & 1) + e;
+                const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -mc));
+                const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], c, -mc));
+                const int a = (cs & 1) * 2 + (e >> 2);
+                if (cs < 2 && (e & 3) == 0) {
+                    rs[a] = p0 + p1;
+                } else {
+                    rs[a] += p0;
+                    rs[a] += p1;
+                }
+                const float2v f2 = {p0, p1};
                 const half2v h2 = __builtin_convertvector(f2, half2v);
                 pf[cs][e] = h2[0];
                 pf[cs][e + 1] = h2[1];
             }
+        st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
         // O^T += V^T . P^T ; the A operand of k-step cs is two transpose reads:
         // keys 16cs + 4h + 0..3 and 16cs + 8 + 4h + 0..3 for lane half h
 #pragma unroll
-        for (int i = 0; i < kDBlocks; ++i)
+        for (int i = 0; i < kDBlocks; ++i) {
+            const _Float16 *vi = vl + v_offset(st, i);
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
-                const half4 lo = lds_read_tr(vl + st.v_addr[i] + 16 * cs * D);
-                const half4 hi = lds_read_tr(vl + st.v_addr[i] + (16 * cs + 8) * D);
+                const half4 lo = lds_read_tr(vi + 16 * cs * D);
+                const half4 hi = lds_read_tr(vi + (16 * cs + 8) * D);
                 const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 st.oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[cs], st.oacc[i], 0, 0, 0);
             }
+        }
     }
 
     __device__ static void run(const Args &a)
@@ -339,9 +373,9 @@ struct Kernel {
         const int n_tiles = (kv_end + kBN - 1) / kBN;
 
         // first tile in flight while Q is fetched
-        LoadOffsets<D> lo;
-        init_load_offsets<D>(lo, kv_row);
-        issue_tile_loads<D>(lo, kbase, vbase, kv_row, 0, L, klds[0], vlds[0]);
+        LoadOffsets<D, W> lo;
+        init_load_offsets<D, W>(lo, kv_row);
+        issue_tile_loads<D, W>(lo, kbase, vbase, kv_row, 0, L, klds[0], vlds[0]);
 
         State st;
         const int wq0 = q0 + 32 * wave;
@@ -357,18 +391,15 @@ struct Kernel {
         st.m = -__builtin_huge_valf();
         st.l = 0.0f;
         // K: row = 32*kb + col, logical chunk 2s + half
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) st.k_addr[s] = col * D + 8 * k_chunk<D>(col, 2 * s + half);
-        // V transpose read: 16-lane group gg = lane/16 (d half gg%2, key half gg/2),
-        // j = lane%16 -> row 4*(gg/2) + j/4 (+ 16*cs [+ 8]), d = 32*i + 16*(gg%2) + 4*(j%4)
+        st.k_base = col * D + 8 * k_chunk<D>(col, half);
+        // V transpose read: 16-lane group gg = lane/16 (d half gg%2, key half
+        // gg/2), j = lane%16 -> row 4*(gg/2) + j/4 (+ 16*cs [+ 8]),
+        // d = 32*i + 16*(gg%2) + 4*(j%4)
         {
             const int gg = lane >> 4, j = lane & 15;
             const int row = 4 * (gg >> 1) + (j >> 2);
-#pragma unroll
-            for (int i = 0; i < kDBlocks; ++i) {
-                const int d = 32 * i + 16 * (gg & 1) + 4 * (j & 3);
-                st.v_addr[i] = row * D + 8 * v_chunk<D>(row, d >> 3) + (d & 7);
-            }
+            const int d = 16 * (gg & 1) + 4 * (j & 3);
+            st.v_base = row * D + 8 * v_chunk<D>(row, d >> 3) + (d & 7);
         }
 
         const float c = a.scale_log2;
@@ -387,10 +418,10 @@ struct Kernel {
             for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    const float2v lo = {st.oacc[i][4 * rb + 0] * inv, st.oacc[i][4 * rb + 1] * inv};
-                    const float2v hi = {st.oacc[i][4 * rb + 2] * inv, st.oacc[i][4 * rb + 3] * inv};
-                    const half2v hl = __builtin_convertvector(lo, half2v);
-                    const half2v hh = __builtin_convertvector(hi, half2v);
+                    const float2v lo2 = {st.oacc[i][4 * rb + 0] * inv, st.oacc[i][4 * rb + 1] * inv};
+                    const float2v hi2 = {st.oacc[i][4 * rb + 2] * inv, st.oacc[i][4 * rb + 3] * inv};
+                    const half2v hl = __builtin_convertvector(lo2, half2v);
+                    const half2v hh = __builtin_convertvector(hi2, half2v);
                     const half4 out = {hl[0], hl[1], hh[0], hh[1]};
                     *(half4 *)(orow + 32 * i + 8 * rb + 4 * half) = out;
                 }
@@ -402,37 +433,43 @@ struct Kernel {
     // One K/V tile: wait for its loads, barrier, start the next tile's loads
     // into the other buffer, compute.  BUF is the buffer tile t lives in.
     template <int BUF>
-    __device__ __forceinline__ static void step(State &st, const LoadOffsets<D> &lo,
-                                                const _Float16 *kbase,
-                                                const _Float16 *vbase, int64_t kv_row, int t,
-                                                int n_tiles, int L, int wq0, int qi, float c,
+    __device__ __forceinline__ static void step(State &st, const LoadOffsets<D, W> &lo,
+                                                const _Float16 *kbase, const _Float16 *vbase,
+                                                int64_t kv_row, int t, int n_tiles, int L,
+                                                int wq0, int qi, float c,
                                                 _Float16 (*klds)[G::kTile],
                                                 _Float16 (*vlds)[G::kTile])
     {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t have landed
         __syncthreads();                // ... and every wave's; tile t-1 fully consumed
         if (t + 1 < n_tiles)
-            issue_tile_loads<D>(lo, kbase, vbase, kv_row, (t + 1) * kBN, L, klds[BUF ^ 1],
-                                vlds[BUF ^ 1]);
+            issue_tile_loads<D, W>(lo, kbase, vbase, kv_row, (t + 1) * kBN, L, klds[BUF ^ 1],
+                                   vlds[BUF ^ 1]);
         const int k0 = t * kBN;
         // a wavefront whose 32 queries all precede this tile has nothing to do
         if (!CAUSAL || k0 <= wq0 + 31) tile(st, klds[BUF], vlds[BUF], k0, L, wq0, qi, c);
     }
 };
 
-template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+template <int D, bool CAUSAL, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W),
                           amdgpu_waves_per_eu(2, 2))) void
 fa_fwd_kernel(const Args a)
 {
-    Kernel<D, CAUSAL>::run(a);
+    Kernel<D, CAUSAL, W>::run(a);
 }
 
 template <int D, bool CAUSAL>
-int launch(const Args &args, hipStream_t stream)
+int launch(Args args, hipStream_t stream)
 {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3(args.n_items), dim3(kThreads), 0, stream,
-                       args);
+    constexpr int W = CAUSAL ? 4 : 8;
+    using K = Kernel<D, CAUSAL, W>;
+    args.n_qblocks = (args.L + K::kBM - 1) / K::kBM;
+    const int64_t items = (int64_t)args.n_items * args.n_qblocks;  // n_items holds B*H here
+    if (items > 0x7fffffff) return FA_ERR_SHAPE;
+    args.n_items = (int)items;
+    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, W>), dim3(args.n_items), dim3(K::kThreads), 0,
+                       stream, args);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -440,6 +477,10 @@ int launch(const Args &args, hipStream_t stream)
 
 int launch_forward(const Problem &p, hipStream_t stream)
 {
+    // per-lane tile offsets are 32-bit: a tile of kBN K/V rows must span < 2 GiB
+    if ((int64_t)p.Hkv * p.D * 2 * kBN > 0x7fffffff) return FA_ERR_SHAPE;
+    const int64_t bh = (int64_t)p.B * p.H;
+    if (bh > 0x7fffffff) return FA_ERR_SHAPE;
     Args a;
     a.q = (const _Float16 *)p.q;
     a.k = (const _Float16 *)p.k;
@@ -450,12 +491,8 @@ int launch_forward(const Problem &p, hipStream_t stream)
     a.H = p.H;
     a.Hkv = p.Hkv;
     a.groups = p.H / p.Hkv;
-    a.n_qblocks = (p.L + kBM - 1) / kBM;
-    int64_t items = (int64_t)p.B * p.H * a.n_qblocks;
-    if (items > 0x7fffffff) return FA_ERR_SHAPE;
-    // per-lane tile offsets are 32-bit: a tile of kBN K/V rows must span < 2 GiB
-    if ((int64_t)p.Hkv * p.D * 2 * kBN > 0x7fffffff) return FA_ERR_SHAPE;
-    a.n_items = (int)items;
+    a.n_qblocks = 0;
+    a.n_items = (int)bh;
     a.scale = p.scale;
     a.scale_log2 = p.scale * 1.4426950408889634f;
     if (p.D == 64) return p.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
