@@ -247,19 +247,19 @@ struct Kernel {
         const int half = (threadIdx.x & 63) >> 5;
 
         // S^T = K . Q^T for the 64 keys of the tile, as two 32-key blocks;
-        // the next k-step's K fragments are read during the current one
+        // every K fragment of the tile is requested before the first MFMA so
+        // LDS latency is paid once per tile, not once per k-step
         floatx16 sacc[2] = {floatx16{}, floatx16{}};
-        half8 ka[2][2];
-        ka[0][0] = lds_read16(kl + k_offset(st, 0));
-        ka[0][1] = lds_read16(kl + k_offset(st, 0) + 32 * D);
+        half8 ka[kSteps][2];
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-            if (s + 1 < kSteps) {
-                ka[(s + 1) & 1][0] = lds_read16(kl + k_offset(st, s + 1));
-                ka[(s + 1) & 1][1] = lds_read16(kl + k_offset(st, s + 1) + 32 * D);
-            }
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s & 1][0], st.qf[s], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s & 1][1], st.qf[s], sacc[1], 0, 0, 0);
+            ka[s][0] = lds_read16(kl + k_offset(st, s));
+            ka[s][1] = lds_read16(kl + k_offset(st, s) + 32 * D);
+        }
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s][0], st.qf[s], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s][1], st.qf[s], sacc[1], 0, 0, 0);
         }
 
         // mask: keys past the sequence end, and keys after the query (causal).
@@ -302,8 +302,10 @@ struct Kernel {
         const float mc = st.m * c;
 
         // P = exp2(S*c - m*c) as fp16 B operands (round-to-nearest-even), one
-        // per 16-key k-step, and the tile's row sum in four partial sums
-        // (partial sum a = 2(cs&1) + e/4 is first written at cs < 2, e in {0,4})
+        // per 16-key k-step.  The row sum adds up exactly those fp16 values
+        // (the weights the P.V product applies), two per v_dot2_f32_f16 into
+        // fp32, in four partial sums (partial sum a = 2(cs&1) + e/4 is first
+        // written at cs < 2, e in {0,4})
         half8 pf[4];
         float rs[4];
 #pragma unroll
@@ -314,31 +316,36 @@ struct Kernel {
                 const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -mc));
                 const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], c, -mc));
                 const int a = (cs & 1) * 2 + (e >> 2);
-                if (cs < 2 && (e & 3) == 0) {
-                    rs[a] = p0 + p1;
-                } else {
-                    rs[a] += p0;
-                    rs[a] += p1;
-                }
                 const float2v f2 = {p0, p1};
                 const half2v h2 = __builtin_convertvector(f2, half2v);
+                const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+                if (cs < 2 && (e & 3) == 0) rs[a] = __builtin_amdgcn_fdot2(h2, ones, 0.0f, false);
+                else rs[a] = __builtin_amdgcn_fdot2(h2, ones, rs[a], false);
                 pf[cs][e] = h2[0];
                 pf[cs][e + 1] = h2[1];
             }
         st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
         // O^T += V^T . P^T ; the A operand of k-step cs is two transpose reads:
-        // keys 16cs + 4h + 0..3 and 16cs + 8 + 4h + 0..3 for lane half h
-#pragma unroll
-        for (int i = 0; i < kDBlocks; ++i) {
+        // keys 16cs + 4h + 0..3 and 16cs + 8 + 4h + 0..3 for lane half h.  The
+        // reads of d block i+1 are in flight during the MFMAs of block i.
+        half8 vbuf[2][4];
+        auto vload = [&](int i, half8 (&dst)[4]) {
             const _Float16 *vi = vl + v_offset(st, i);
 #pragma unroll
             for (int cs = 0; cs < 4; ++cs) {
                 const half4 lo = lds_read_tr(vi + 16 * cs * D);
                 const half4 hi = lds_read_tr(vi + (16 * cs + 8) * D);
-                const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                st.oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[cs], st.oacc[i], 0, 0, 0);
+                dst[cs] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
+        };
+        vload(0, vbuf[0]);
+#pragma unroll
+        for (int i = 0; i < kDBlocks; ++i) {
+            if (i + 1 < kDBlocks) vload(i + 1, vbuf[(i + 1) & 1]);
+#pragma unroll
+            for (int cs = 0; cs < 4; ++cs)
+                st.oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vbuf[i & 1][cs], pf[cs], st.oacc[i], 0, 0, 0);
         }
     }
 
