@@ -68,6 +68,8 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kBN = 64;               // keys per K/V tile
+constexpr int kKB = kBN / 32;         // 32-key blocks of S^T per tile
+constexpr int kCS = kBN / 16;         // 16-key k-steps of the P.V product per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
 
@@ -241,26 +243,39 @@ struct Kernel {
     __device__ __forceinline__ static int k_offset(const State &st, int s) { return st.k_base ^ (16 * s); }
     __device__ __forceinline__ static int v_offset(const State &st, int i) { return st.v_base ^ (32 * i); }
 
-    __device__ __forceinline__ static void tile(State &st, const _Float16 *kl, const _Float16 *vl,
-                                                int k0, int L, int wq0, int qi, float c)
+    // S^T = K . Q^T for the 64 keys of the tile, as two 32-key blocks;
+    // every K fragment of the tile is requested before the first MFMA so LDS
+    // latency is paid once per tile, not once per k-step
+    static constexpr int kAhead = kSteps;
+
+    __device__ __forceinline__ static void s_product(floatx16 (&sacc)[kKB], const State &st,
+                                                     const _Float16 *kl)
+    {
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) sacc[kb] = floatx16{};
+        half8 ka[kSteps][kKB];
+#pragma unroll
+        for (int s = 0; s < kAhead; ++s)
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb) ka[s][kb] = lds_read16(kl + k_offset(st, s) + 32 * kb * D);
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            if (s + kAhead < kSteps)
+#pragma unroll
+                for (int kb = 0; kb < kKB; ++kb)
+                    ka[s + kAhead][kb] = lds_read16(kl + k_offset(st, s + kAhead) + 32 * kb * D);
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb)
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s][kb], st.qf[s], sacc[kb], 0, 0, 0);
+        }
+    }
+
+    // mask, row maximum, lazy rescale, and P = exp2(S*c - m*c) as fp16 B
+    // operands of the P.V product (one per 16-key k-step), with the row sum
+    __device__ __forceinline__ static void softmax(State &st, floatx16 (&sacc)[kKB], half8 (&pf)[kCS],
+                                                   int k0, int L, int wq0, int qi, float c)
     {
         const int half = (threadIdx.x & 63) >> 5;
-
-        // S^T = K . Q^T for the 64 keys of the tile, as two 32-key blocks;
-        // every K fragment of the tile is requested before the first MFMA so
-        // LDS latency is paid once per tile, not once per k-step
-        floatx16 sacc[2] = {floatx16{}, floatx16{}};
-        half8 ka[kSteps][2];
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            ka[s][0] = lds_read16(kl + k_offset(st, s));
-            ka[s][1] = lds_read16(kl + k_offset(st, s) + 32 * D);
-        }
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s][0], st.qf[s], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s][1], st.qf[s], sacc[1], 0, 0, 0);
-        }
 
         // mask: keys past the sequence end, and keys after the query (causal).
         // Register r of block kb holds key k0 + 4*half + 32kb + 8(r/4) + r%4,
@@ -272,18 +287,22 @@ struct Kernel {
                 bound = cb < bound ? cb : bound;
             }
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (32 * kb + 8 * (r >> 2) + (r & 3) >= bound) sacc[kb][r] = -__builtin_huge_valf();
         }
 
-        // row maximum of the tile, both lane halves
-        float mx = sacc[0][0];
+        // row maximum of the tile, both lane halves: four independent chains
+        // (short dependency chains), then one cross-half exchange
+        float mq[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int a = 0; a < 4; ++a) mq[a] = sacc[0][a];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+            for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], sacc[kb][r]);
+        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
         mx = pair_max(mx);
 
         // lazy rescale: raise the reference maximum only when some row's
@@ -306,10 +325,9 @@ struct Kernel {
         // (the weights the P.V product applies), two per v_dot2_f32_f16 into
         // fp32, in four partial sums (partial sum a = 2(cs&1) + e/4 is first
         // written at cs < 2, e in {0,4})
-        half8 pf[4];
         float rs[4];
 #pragma unroll
-        for (int cs = 0; cs < 4; ++cs)
+        for (int cs = 0; cs < kCS; ++cs)
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const int kb = cs >> 1, r = 8 * (cs & 1) + e;
@@ -325,28 +343,45 @@ struct Kernel {
                 pf[cs][e + 1] = h2[1];
             }
         st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    }
 
-        // O^T += V^T . P^T ; the A operand of k-step cs is two transpose reads:
-        // keys 16cs + 4h + 0..3 and 16cs + 8 + 4h + 0..3 for lane half h.  The
-        // reads of d block i+1 are in flight during the MFMAs of block i.
-        half8 vbuf[2][4];
-        auto vload = [&](int i, half8 (&dst)[4]) {
-            const _Float16 *vi = vl + v_offset(st, i);
-#pragma unroll
-            for (int cs = 0; cs < 4; ++cs) {
-                const half4 lo = lds_read_tr(vi + 16 * cs * D);
-                const half4 hi = lds_read_tr(vi + (16 * cs + 8) * D);
-                dst[cs] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
+    // O^T += V^T . P^T ; the A operand of k-step cs is two transpose reads:
+    // keys 16cs + 4h + 0..3 and 16cs + 8 + 4h + 0..3 for lane half h.  The
+    // reads of d block i+1 are in flight during the MFMAs of block i.
+    __device__ __forceinline__ static void pv_product(State &st, const half8 (&pf)[kCS],
+                                                      const _Float16 *vl)
+    {
+        // MFMA n = (d block i, k-step cs) = (n / kCS, n % kCS); its operand is
+        // read kVAhead MFMAs earlier
+        constexpr int kN = kDBlocks * kCS;
+        constexpr int kVAhead = 4;
+        half8 va[kN];
+        auto vload = [&](int n) {
+            const _Float16 *vi = vl + v_offset(st, n / kCS);
+            const int cs = n % kCS;
+            const half4 lo = lds_read_tr(vi + 16 * cs * D);
+            const half4 hi = lds_read_tr(vi + (16 * cs + 8) * D);
+            va[n] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         };
-        vload(0, vbuf[0]);
 #pragma unroll
-        for (int i = 0; i < kDBlocks; ++i) {
-            if (i + 1 < kDBlocks) vload(i + 1, vbuf[(i + 1) & 1]);
+        for (int n = 0; n < kVAhead; ++n) vload(n);
 #pragma unroll
-            for (int cs = 0; cs < 4; ++cs)
-                st.oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vbuf[i & 1][cs], pf[cs], st.oacc[i], 0, 0, 0);
+        for (int n = 0; n < kN; ++n) {
+            if (n + kVAhead < kN) vload(n + kVAhead);
+            st.oacc[n / kCS] =
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pf[n % kCS], st.oacc[n / kCS], 0, 0, 0);
         }
+    }
+
+    // one whole K/V tile for one wavefront
+    __device__ __forceinline__ static void tile(State &st, const _Float16 *kl, const _Float16 *vl,
+                                                int k0, int L, int wq0, int qi, float c)
+    {
+        floatx16 sacc[kKB];
+        half8 pf[kCS];
+        s_product(sacc, st, kl);
+        softmax(st, sacc, pf, k0, L, wq0, qi, c);
+        pv_product(st, pf, vl);
     }
 
     __device__ static void run(const Args &a)
