@@ -67,9 +67,8 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBN = 64;               // keys per K/V tile
-constexpr int kKB = kBN / 32;         // 32-key blocks of S^T per tile
-constexpr int kCS = kBN / 16;         // 16-key k-steps of the P.V product per tile
+constexpr int kBN = 64;               // keys per K/V tile in LDS
+constexpr int kSB = 32;               // keys per score block (one 32x32 accumulator)
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
 
@@ -173,33 +172,28 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t off, _Float16 *
                      : "memory");
 }
 
-// Issue this wave's share of the direct loads of the K and V tiles that start
-// at key k0.  A tile reaching past L loads row L-1 in place of the missing
-// rows (finite data that the mask hides).
-template <int D, int W>
-__device__ __forceinline__ void issue_tile_loads(const LoadOffsets<D, W> &lo,
-                                                 const _Float16 *kbase, const _Float16 *vbase,
-                                                 int64_t kv_row, int k0, int L, _Float16 *klds,
-                                                 _Float16 *vlds)
+// Issue this wave's share of the direct loads of the K (or V) tile that
+// starts at key k0.  A tile reaching past L loads row L-1 in place of the
+// missing rows (finite data that the mask hides); rows before key 0 (the
+// first K tile starts at key -32) are not loaded and never read.
+template <int D, int W, bool IS_V>
+__device__ __forceinline__ void issue_loads(const LoadOffsets<D, W> &lo, const _Float16 *base,
+                                            int64_t kv_row, int k0, int L, _Float16 *lds)
 {
     using G = Geo<D, W>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const char *kt = (const char *)(kbase + (int64_t)k0 * kv_row);
-    const char *vt = (const char *)(vbase + (int64_t)k0 * kv_row);
+    const char *tile = (const char *)(base + (int64_t)k0 * kv_row);
     const bool full = k0 + kBN <= L;
 #pragma unroll
     for (int n = 0; n < G::kLoadsPerWave; ++n) {
         const int blk = G::kLoadsPerWave * wave + n;
-        uint32_t ko = lo.k[n], vo = lo.v[n];
+        if (k0 + G::kRowsPerLoad * blk < 0) continue;  // whole instruction before key 0
+        uint32_t off = IS_V ? lo.v[n] : lo.k[n];
         if (!full) {
             const int over = k0 + load_row<D, W>(n) - (L - 1);  // rows past the end re-read row L-1
-            if (over > 0) {
-                ko -= (uint32_t)(2 * over * kv_row);
-                vo -= (uint32_t)(2 * over * kv_row);
-            }
+            if (over > 0) off -= (uint32_t)(2 * over * kv_row);
         }
-        dma16(kt, ko, klds + 512 * blk);
-        dma16(vt, vo, vlds + 512 * blk);
+        dma16(tile, off, lds + 512 * blk);
     }
 }
 
@@ -226,12 +220,16 @@ struct Kernel {
     static constexpr int kBM = 32 * W;       // query rows per work item
     static constexpr int kSteps = D / 16;    // k-steps of S^T = K.Q^T
     static constexpr int kDBlocks = D / 32;  // 32-row blocks of O^T
+    static constexpr int kCS = kSB / 16;     // 16-key k-steps of P.V per score block
+    static constexpr int kPairs = 8;         // score pairs per lane per score block
+    static constexpr int kPairsA = 6;        // pairs exponentiated beside the S product
 
     // per-lane state of one wavefront
     struct State {
         half8 qf[kSteps];
         floatx16 oacc[kDBlocks];
         float m;     // reference row maximum (raw score units)
+        float mc;    // m * c, c = scale * log2(e)
         float l;     // running row sum, this lane's keys
         int k_base;  // LDS half offset of this lane's K read at k-step 0
         int v_base;  // LDS half offset of this lane's V transpose read at d block 0
@@ -243,70 +241,97 @@ struct Kernel {
     __device__ __forceinline__ static int k_offset(const State &st, int s) { return st.k_base ^ (16 * s); }
     __device__ __forceinline__ static int v_offset(const State &st, int i) { return st.v_base ^ (32 * i); }
 
-    // S^T = K . Q^T for the 64 keys of the tile, as two 32-key blocks;
-    // every K fragment of the tile is requested before the first MFMA so LDS
-    // latency is paid once per tile, not once per k-step
-    static constexpr int kAhead = kSteps;
-
-    __device__ __forceinline__ static void s_product(floatx16 (&sacc)[kKB], const State &st,
-                                                     const _Float16 *kl)
+    // A operand of S^T for k-step s; kl points at the block's first K row
+    __device__ __forceinline__ static half8 kfrag(const State &st, const _Float16 *kl, int s)
     {
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) sacc[kb] = floatx16{};
-        half8 ka[kSteps][kKB];
-#pragma unroll
-        for (int s = 0; s < kAhead; ++s)
-#pragma unroll
-            for (int kb = 0; kb < kKB; ++kb) ka[s][kb] = lds_read16(kl + k_offset(st, s) + 32 * kb * D);
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            if (s + kAhead < kSteps)
-#pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
-                    ka[s + kAhead][kb] = lds_read16(kl + k_offset(st, s + kAhead) + 32 * kb * D);
-#pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s][kb], st.qf[s], sacc[kb], 0, 0, 0);
-        }
+        return lds_read16(kl + k_offset(st, s));
     }
 
-    // mask, row maximum, lazy rescale, and P = exp2(S*c - m*c) as fp16 B
-    // operands of the P.V product (one per 16-key k-step), with the row sum
-    __device__ __forceinline__ static void softmax(State &st, floatx16 (&sacc)[kKB], half8 (&pf)[kCS],
-                                                   int k0, int L, int wq0, int qi, float c)
+    // A operand of O^T for d block i and k-step cs; vl points at the block's
+    // first V row.  Two transpose reads: keys 16cs + 4h + 0..3 and
+    // 16cs + 8 + 4h + 0..3 for lane half h.
+    __device__ __forceinline__ static half8 vfrag(const State &st, const _Float16 *vl, int i, int cs)
+    {
+        const _Float16 *p = vl + v_offset(st, i) + 16 * cs * D;
+        const half4 lo = lds_read_tr(p);
+        const half4 hi = lds_read_tr(p + 8 * D);
+        return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+
+    // the block at key k0 holds keys past the sequence end or after a query
+    __device__ __forceinline__ static bool needs_mask(int k0, int L, int wq0)
+    {
+        return (k0 + kSB > L) || (CAUSAL && k0 + kSB - 1 > wq0);
+    }
+
+    // Mask keys past the sequence end, and keys after the query (causal).
+    // Register r holds key k0 + 4*half + 8(r/4) + r%4, so one per-lane bound
+    // decides every element.
+    __device__ __forceinline__ static void mask(floatx16 &sacc, int k0, int L, int qi)
     {
         const int half = (threadIdx.x & 63) >> 5;
-
-        // mask: keys past the sequence end, and keys after the query (causal).
-        // Register r of block kb holds key k0 + 4*half + 32kb + 8(r/4) + r%4,
-        // so one per-lane bound decides every element.
-        if ((k0 + kBN > L) || (CAUSAL && k0 + kBN - 1 > wq0)) {
-            int bound = L - k0 - 4 * half;  // hide offsets >= bound
-            if (CAUSAL) {
-                const int cb = qi - k0 - 4 * half + 1;
-                bound = cb < bound ? cb : bound;
-            }
-#pragma unroll
-            for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 8 * (r >> 2) + (r & 3) >= bound) sacc[kb][r] = -__builtin_huge_valf();
+        int bound = L - k0 - 4 * half;  // hide offsets >= bound
+        if (CAUSAL) {
+            const int cb = qi - k0 - 4 * half + 1;
+            bound = cb < bound ? cb : bound;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) >= bound) sacc[r] = -__builtin_huge_valf();
+    }
 
-        // row maximum of the tile, both lane halves: four independent chains
-        // (short dependency chains), then one cross-half exchange
-        float mq[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) mq[a] = sacc[0][a];
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int r = (kb == 0 ? 4 : 0); r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], sacc[kb][r]);
-        float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-        mx = pair_max(mx);
+    // Row maximum of a score block over both lane halves -- a tree of
+    // 3-input maxima, then one cross-half exchange -- in stages that can be
+    // spread between other instructions.
+    struct MaxTree {
+        static constexpr int kStages = 5;
+        float a, b, d, e, f, g, h, mx;
+        __device__ __forceinline__ void stage(int i, const floatx16 &x)
+        {
+            switch (i) {
+            case 0:
+                a = fmaxf(fmaxf(x[0], x[1]), x[2]);
+                b = fmaxf(fmaxf(x[3], x[4]), x[5]);
+                break;
+            case 1:
+                d = fmaxf(fmaxf(x[6], x[7]), x[8]);
+                e = fmaxf(fmaxf(x[9], x[10]), x[11]);
+                break;
+            case 2:
+                f = fmaxf(fmaxf(x[12], x[13]), x[14]);
+                g = fmaxf(fmaxf(a, b), d);
+                break;
+            case 3: h = fmaxf(fmaxf(e, f), x[15]); break;
+            default: mx = pair_max(fmaxf(g, h)); break;
+            }
+        }
+    };
 
-        // lazy rescale: raise the reference maximum only when some row's
-        // maximum outgrew it by more than 2^kRescaleLog2
+    __device__ __forceinline__ static float block_max(const floatx16 &x)
+    {
+        MaxTree t;
+#pragma unroll
+        for (int i = 0; i < MaxTree::kStages; ++i) t.stage(i, x);
+        return t.mx;
+    }
+
+    // S^T = K . Q^T for one score block, no other work in between
+    __device__ __forceinline__ static void s_product(floatx16 &sacc, const State &st, const _Float16 *kl)
+    {
+        half8 ka[kSteps];
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) ka[s] = kfrag(st, kl, s);
+        sacc = floatx16{};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s], st.qf[s], sacc, 0, 0, 0);
+    }
+
+    // Lazy rescale: raise the reference maximum only when some row's block
+    // maximum outgrew it by more than 2^kRescaleLog2 (decided for the whole
+    // wavefront); O and l are scaled by the same factor.
+    __device__ __forceinline__ static void rescale(State &st, float mx, float c)
+    {
         const bool grow = (mx - st.m) * c > kRescaleLog2;
         if (__builtin_amdgcn_ballot_w64(grow)) {
             const float m_new = fmaxf(st.m, mx);
@@ -318,70 +343,179 @@ struct Kernel {
                 for (int r = 0; r < 16; ++r) st.oacc[i][r] *= sf;
             st.m = m_new;
         }
-        const float mc = st.m * c;
-
-        // P = exp2(S*c - m*c) as fp16 B operands (round-to-nearest-even), one
-        // per 16-key k-step.  The row sum adds up exactly those fp16 values
-        // (the weights the P.V product applies), two per v_dot2_f32_f16 into
-        // fp32, in four partial sums (partial sum a = 2(cs&1) + e/4 is first
-        // written at cs < 2, e in {0,4})
-        float rs[4];
-#pragma unroll
-        for (int cs = 0; cs < kCS; ++cs)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const int kb = cs >> 1, r = 8 * (cs & 1) + e;
-                const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -mc));
-                const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], c, -mc));
-                const int a = (cs & 1) * 2 + (e >> 2);
-                const float2v f2 = {p0, p1};
-                const half2v h2 = __builtin_convertvector(f2, half2v);
-                const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-                if (cs < 2 && (e & 3) == 0) rs[a] = __builtin_amdgcn_fdot2(h2, ones, 0.0f, false);
-                else rs[a] = __builtin_amdgcn_fdot2(h2, ones, rs[a], false);
-                pf[cs][e] = h2[0];
-                pf[cs][e + 1] = h2[1];
-            }
-        st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        st.mc = st.m * c;
     }
 
-    // O^T += V^T . P^T ; the A operand of k-step cs is two transpose reads:
-    // keys 16cs + 4h + 0..3 and 16cs + 8 + 4h + 0..3 for lane half h.  The
-    // reads of d block i+1 are in flight during the MFMAs of block i.
-    __device__ __forceinline__ static void pv_product(State &st, const half8 (&pf)[kCS],
-                                                      const _Float16 *vl)
+    // P = exp2(S*c - m*c) for score pair p (registers 2p, 2p+1), rounded to
+    // fp16 (round-to-nearest-even) into the B operand of k-step cs = p/4 of
+    // the P.V product at position 2(p%4).  The row sum adds exactly those
+    // fp16 values (the weights the P.V product applies), two per
+    // v_dot2_f32_f16, into two fp32 partial sums.
+    __device__ __forceinline__ static void exp_pair(const floatx16 &sc, half8 (&pf)[kCS], float (&rs)[2],
+                                                    int p, float mc, float c)
     {
-        // MFMA n = (d block i, k-step cs) = (n / kCS, n % kCS); its operand is
-        // read kVAhead MFMAs earlier
+        const int r = 2 * p, cs = r >> 3, e = r & 7;
+        const float p0 = exp2_fast(__builtin_fmaf(sc[r], c, -mc));
+        const float p1 = exp2_fast(__builtin_fmaf(sc[r + 1], c, -mc));
+        const float2v f2 = {p0, p1};
+        const half2v h2 = __builtin_convertvector(f2, half2v);
+        const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+        rs[p & 1] = __builtin_amdgcn_fdot2(h2, ones, rs[p & 1], false);
+        pf[cs][e] = h2[0];
+        pf[cs][e + 1] = h2[1];
+        // keep the pair where it stands in the schedule: without a use here
+        // the compiler sinks it towards its first MFMA
+        __asm__ volatile("" ::"v"(h2), "v"(rs[p & 1]));
+    }
+
+    // One pipelined step for score block u (scores sc, reference maximum
+    // already taken): the S product of block u+1 (into sn, when NEXT) runs
+    // interleaved with the exponentials of block u, then the P.V product of
+    // block u runs beside the last exponentials, and the row maximum of
+    // block u+1 (masked first when mask_next) is returned in mx_next.  The
+    // matrix unit always has work that does not wait on the vector ALU and
+    // vice versa.  kl: first K row of block u+1, vl: first V row of block u.
+    template <bool NEXT>
+    __device__ __forceinline__ static void body(State &st, const floatx16 &sc, floatx16 &sn,
+                                                const _Float16 *kl, const _Float16 *vl,
+                                                bool mask_next, int k0_next, int L, int qi, float c,
+                                                float &mx_next)
+    {
+        half8 pf[kCS];
+        float rs[2] = {0.0f, 0.0f};
+        const float mc = st.mc;
+
+        // S(u+1) = K(u+1) . Q^T beside pairs [0, kPairsA) of block u; K
+        // fragments are requested kAhead k-steps before their MFMAs
+        if constexpr (NEXT) {
+            constexpr int kAhead = kSteps < 4 ? kSteps : 4;
+            half8 ka[kSteps];
+#pragma unroll
+            for (int s = 0; s < kAhead; ++s) ka[s] = kfrag(st, kl, s);
+            sn = floatx16{};
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                if (s + kAhead < kSteps) ka[s + kAhead] = kfrag(st, kl, s + kAhead);
+                sn = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s], st.qf[s], sn, 0, 0, 0);
+#pragma unroll
+                for (int p = kPairsA * s / kSteps; p < kPairsA * (s + 1) / kSteps; ++p)
+                    exp_pair(sc, pf, rs, p, mc, c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < kPairsA; ++p) exp_pair(sc, pf, rs, p, mc, c);
+        }
+
+        // O^T += V^T . P^T, k-step-major so that the operand holding the
+        // remaining pairs is needed last; V operands kVAhead MFMAs ahead.
+        // From MFMA 2 on (S(u+1) has completed by then) the row maximum of
+        // block u+1 is taken in stages beside the MFMAs.
         constexpr int kN = kDBlocks * kCS;
         constexpr int kVAhead = 4;
+        constexpr int kMaxFrom = 2;
         half8 va[kN];
-        auto vload = [&](int n) {
-            const _Float16 *vi = vl + v_offset(st, n / kCS);
-            const int cs = n % kCS;
-            const half4 lo = lds_read_tr(vi + 16 * cs * D);
-            const half4 hi = lds_read_tr(vi + (16 * cs + 8) * D);
-            va[n] = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        };
+        MaxTree mt;
 #pragma unroll
-        for (int n = 0; n < kVAhead; ++n) vload(n);
+        for (int n = 0; n < kVAhead; ++n) va[n] = vfrag(st, vl, n % kDBlocks, n / kDBlocks);
 #pragma unroll
         for (int n = 0; n < kN; ++n) {
-            if (n + kVAhead < kN) vload(n + kVAhead);
-            st.oacc[n / kCS] =
-                __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pf[n % kCS], st.oacc[n / kCS], 0, 0, 0);
+            if (n + kVAhead < kN) va[n + kVAhead] = vfrag(st, vl, (n + kVAhead) % kDBlocks, (n + kVAhead) / kDBlocks);
+            if (kPairsA + n < kPairs) exp_pair(sc, pf, rs, kPairsA + n, mc, c);
+            if constexpr (NEXT) {
+                if (n == kMaxFrom && mask_next) mask(sn, k0_next, L, qi);
+                if (n >= kMaxFrom) {
+                    constexpr int kSlots = kN - kMaxFrom;
+#pragma unroll
+                    for (int g = MaxTree::kStages * (n - kMaxFrom) / kSlots;
+                         g < MaxTree::kStages * (n - kMaxFrom + 1) / kSlots; ++g)
+                        mt.stage(g, sn);
+                }
+            }
+            st.oacc[n % kDBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pf[n / kDBlocks],
+                                                                            st.oacc[n % kDBlocks], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        st.l += rs[0] + rs[1];
+        if constexpr (NEXT) mx_next = mt.mx;
     }
 
-    // one whole K/V tile for one wavefront
-    __device__ __forceinline__ static void tile(State &st, const _Float16 *kl, const _Float16 *vl,
-                                                int k0, int L, int wq0, int qi, float c)
+    // Score block u (keys 32u..32u+31) followed by block u+1.  Under the
+    // causal mask a block past a wavefront's diagonal is still computed, with
+    // every score masked to -inf: its weights are exactly 0 and the reference
+    // maximum is unchanged, so the result is the same as skipping it, and
+    // every wavefront of the workgroup runs the same straight-line code.
+    __device__ __forceinline__ static void block_next(State &st, const floatx16 &sc, floatx16 &sn,
+                                                      const _Float16 *kl, const _Float16 *vl, int u,
+                                                      int L, int wq0, int qi, float c)
     {
-        floatx16 sacc[kKB];
-        half8 pf[kCS];
-        s_product(sacc, st, kl);
-        softmax(st, sacc, pf, k0, L, wq0, qi, c);
-        pv_product(st, pf, vl);
+        const int k0n = kSB * (u + 1);
+        float mx;
+        body<true>(st, sc, sn, kl, vl, needs_mask(k0n, L, wq0), k0n, L, qi, c, mx);
+        rescale(st, mx, c);
+    }
+
+    // the last score block of the work item
+    __device__ __forceinline__ static void block_last(State &st, const floatx16 &sc, floatx16 &sn,
+                                                      const _Float16 *vl, int L, int qi, float c)
+    {
+        float mx;
+        body<false>(st, sc, sn, nullptr, vl, false, 0, L, qi, c, mx);
+    }
+
+    // LDS tile t (P = t % 2) covers score blocks u = 2t (scores in sa) and
+    // 2t+1 (scores in sb).  V tile t holds keys 64t..64t+63 in vlds[t % 2];
+    // K tile t holds keys 64t+32..64t+95 in klds[(t+1) % 2] -- 32 keys ahead,
+    // so the two S products of the tile (blocks 2t+1 and 2t+2) read the one
+    // K tile that the P.V products' V tile is paired with.  At the barrier
+    // K(t) and V(t) have landed and every wavefront is done with K(t-1) and
+    // V(t-1), whose buffers then receive K(t+1) and V(t+1).
+    template <int P>
+    __device__ __forceinline__ static void tile_start(const LoadOffsets<D, W> &lo, const _Float16 *kbase,
+                                                      const _Float16 *vbase, int64_t kv_row, int t,
+                                                      int n_tiles, int n_blocks, int L,
+                                                      _Float16 (*klds)[G::kTile],
+                                                      _Float16 (*vlds)[G::kTile])
+    {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(t), V(t) have landed
+        __syncthreads();                // ... and every wave's
+        if (2 * t + 3 < n_blocks)
+            issue_loads<D, W, false>(lo, kbase, kv_row, kBN * (t + 1) + kSB, L, klds[P]);
+        if (t + 1 < n_tiles) issue_loads<D, W, true>(lo, vbase, kv_row, kBN * (t + 1), L, vlds[P ^ 1]);
+    }
+
+    // a tile whose two blocks both have a successor
+    template <int P>
+    __device__ __forceinline__ static void tile(State &st, floatx16 &sa, floatx16 &sb,
+                                                const LoadOffsets<D, W> &lo, const _Float16 *kbase,
+                                                const _Float16 *vbase, int64_t kv_row, int t,
+                                                int n_tiles, int n_blocks, int L, int wq0, int qi,
+                                                float c, _Float16 (*klds)[G::kTile],
+                                                _Float16 (*vlds)[G::kTile])
+    {
+        tile_start<P>(lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, klds, vlds);
+        const _Float16 *kl = klds[P ^ 1], *vl = vlds[P];
+        block_next(st, sa, sb, kl, vl, 2 * t, L, wq0, qi, c);
+        block_next(st, sb, sa, kl + kSB * D, vl + kSB * D, 2 * t + 1, L, wq0, qi, c);
+    }
+
+    // the final tile: block 2t+1, if it exists, is the last one
+    template <int P>
+    __device__ __forceinline__ static void tile_final(State &st, floatx16 &sa, floatx16 &sb,
+                                                      const LoadOffsets<D, W> &lo, const _Float16 *kbase,
+                                                      const _Float16 *vbase, int64_t kv_row, int t,
+                                                      int n_tiles, int n_blocks, int L, int wq0, int qi,
+                                                      float c, _Float16 (*klds)[G::kTile],
+                                                      _Float16 (*vlds)[G::kTile])
+    {
+        tile_start<P>(lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, klds, vlds);
+        const _Float16 *kl = klds[P ^ 1], *vl = vlds[P];
+        if (2 * t + 1 < n_blocks) {
+            block_next(st, sa, sb, kl, vl, 2 * t, L, wq0, qi, c);
+            block_last(st, sb, sa, vl + kSB * D, L, qi, c);
+        } else {
+            block_last(st, sa, sb, vl, L, qi, c);
+        }
     }
 
     __device__ static void run(const Args &a)
@@ -390,7 +524,8 @@ struct Kernel {
         __shared__ __attribute__((aligned(16))) _Float16 vlds[2][G::kTile];
 
         const int tid = threadIdx.x;
-        const int lane = tid & 63, wave = tid >> 6;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int col = lane & 31, half = lane >> 5;
 
         // ---- work item
@@ -412,12 +547,15 @@ struct Kernel {
         const _Float16 *vbase = a.v + (int64_t)b * L * kv_row + (int64_t)hk * D;
 
         const int kv_end = CAUSAL ? (q0 + kBM < L ? q0 + kBM : L) : L;
+        const int n_blocks = (kv_end + kSB - 1) / kSB;
         const int n_tiles = (kv_end + kBN - 1) / kBN;
 
-        // first tile in flight while Q is fetched
+        // K tile -1 (keys 0..31 in its upper half) and V tile 0 in flight
+        // while Q is fetched
         LoadOffsets<D, W> lo;
         init_load_offsets<D, W>(lo, kv_row);
-        issue_tile_loads<D, W>(lo, kbase, vbase, kv_row, 0, L, klds[0], vlds[0]);
+        issue_loads<D, W, false>(lo, kbase, kv_row, -kSB, L, klds[0]);
+        issue_loads<D, W, true>(lo, vbase, kv_row, 0, L, vlds[0]);
 
         State st;
         const int wq0 = q0 + 32 * wave;
@@ -432,7 +570,7 @@ struct Kernel {
         for (int i = 0; i < kDBlocks; ++i) st.oacc[i] = floatx16{};
         st.m = -__builtin_huge_valf();
         st.l = 0.0f;
-        // K: row = 32*kb + col, logical chunk 2s + half
+        // K: row = col (+ 32 for the upper half of a tile), logical chunk 2s + half
         st.k_base = col * D + 8 * k_chunk<D>(col, half);
         // V transpose read: 16-lane group gg = lane/16 (d half gg%2, key half
         // gg/2), j = lane%16 -> row 4*(gg/2) + j/4 (+ 16*cs [+ 8]),
@@ -443,13 +581,34 @@ struct Kernel {
             const int d = 16 * (gg & 1) + 4 * (j & 3);
             st.v_base = row * D + 8 * v_chunk<D>(row, d >> 3) + (d & 7);
         }
-
         const float c = a.scale_log2;
-        for (int t = 0; t < n_tiles; t += 2) {
-            step<0>(st, lo, kbase, vbase, kv_row, t, n_tiles, L, wq0, qi, c, klds, vlds);
-            if (t + 1 < n_tiles)
-                step<1>(st, lo, kbase, vbase, kv_row, t + 1, n_tiles, L, wq0, qi, c, klds, vlds);
+
+        // prologue: scores and reference maximum of block 0 (every wavefront
+        // sees key 0); K tile 0 in flight
+        floatx16 sa, sb;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (n_blocks > 1) issue_loads<D, W, false>(lo, kbase, kv_row, kSB, L, klds[1]);
+        s_product(sa, st, klds[0] + kSB * D);
+        if (needs_mask(0, L, wq0)) mask(sa, 0, L, qi);
+        rescale(st, block_max(sa), c);
+
+        // tiles t < n_main = n_tiles - 1 have a successor for both blocks;
+        // tile n_tiles - 1 holds the last block
+        const int n_main = (n_blocks - 1) / 2;
+        int t = 0;
+        for (; t + 1 < n_main; t += 2) {
+            tile<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
+            tile<1>(st, sa, sb, lo, kbase, vbase, kv_row, t + 1, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
         }
+        if (t < n_main) {
+            tile<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
+            ++t;
+        }
+        if (t & 1)
+            tile_final<1>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
+        else
+            tile_final<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
 
         // ---- finalise: O = acc / l (guarded as on the page), LSE = scale*m + ln l
         const float lt = pair_sum(st.l);
@@ -470,26 +629,6 @@ struct Kernel {
             if (a.lse && half == 0)
                 a.lse[((int64_t)b * a.H + h) * L + qi] = st.m * a.scale + __logf(lt);
         }
-    }
-
-    // One K/V tile: wait for its loads, barrier, start the next tile's loads
-    // into the other buffer, compute.  BUF is the buffer tile t lives in.
-    template <int BUF>
-    __device__ __forceinline__ static void step(State &st, const LoadOffsets<D, W> &lo,
-                                                const _Float16 *kbase, const _Float16 *vbase,
-                                                int64_t kv_row, int t, int n_tiles, int L,
-                                                int wq0, int qi, float c,
-                                                _Float16 (*klds)[G::kTile],
-                                                _Float16 (*vlds)[G::kTile])
-    {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t have landed
-        __syncthreads();                // ... and every wave's; tile t-1 fully consumed
-        if (t + 1 < n_tiles)
-            issue_tile_loads<D, W>(lo, kbase, vbase, kv_row, (t + 1) * kBN, L, klds[BUF ^ 1],
-                                   vlds[BUF ^ 1]);
-        const int k0 = t * kBN;
-        // a wavefront whose 32 queries all precede this tile has nothing to do
-        if (!CAUSAL || k0 <= wq0 + 31) tile(st, klds[BUF], vlds[BUF], k0, L, wq0, qi, c);
     }
 };
 
