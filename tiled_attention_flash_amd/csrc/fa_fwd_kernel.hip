@@ -33,19 +33,26 @@
 // * K/V tiles of BN = 64 keys travel HBM -> LDS with global_load_lds_dwordx4
 //   (16 bytes per lane, no staging registers), double-buffered with one
 //   workgroup barrier per tile; the next tile's loads fly while the current
-//   one is computed.  The source address of each lane is chosen so that rows
+//   one is computed.  K tiles start 32 keys after V tiles, so that the two
+//   S products a tile's step issues (see below) read the K tile paired with
+//   the V tile.  The source address of each lane is chosen so that rows
 //   land with a 16-byte-chunk XOR swizzle that makes the K reads
 //   (ds_read_b128, 16 rows per LDS cycle) and the V transpose reads (4 rows x
 //   64 bytes per half-wavefront) free of bank conflicts.  Rows past the end
 //   of the sequence load row L-1 instead (finite data that the mask hides).
+// * Software pipeline over score blocks of 32 keys: while the matrix unit
+//   computes S of block u+1, the vector ALU exponentiates block u; P.V of
+//   block u then runs beside the row maximum of block u+1.
 // * Online softmax with a lazy rescale: the reference maximum of a row is
 //   raised (and O, l rescaled) only when some row of the wavefront sees its
 //   maximum grow by more than 2^8 in the exp2 domain; otherwise the stale
 //   maximum keeps every probability <= 256 (well inside fp16's range) and the
 //   final O / l and LSE are unchanged.
-// * Causal: tiles past the block's last query are never visited; the mask
-//   code runs only on tiles that straddle a wavefront's diagonal (or hold the
-//   ragged end of the sequence).
+// * Causal: tiles past the work item's last query are never visited; the
+//   mask code runs only on blocks that straddle a wavefront's diagonal (or
+//   hold the ragged end of the sequence).  Blocks past a wavefront's diagonal
+//   but before the work item's end are computed fully masked (weights 0), so
+//   every wavefront runs the same code.
 // * Grid: one workgroup per (b, kv head, group member, q block) work item;
 //   workgroup ids are remapped so that each of the 8 XCDs (which receive
 //   workgroups round-robin) walks a contiguous range of work items, keeping
