@@ -47,6 +47,39 @@ def measured_traffic(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
+def sample_clock_power(step, seconds: float = 1.5):
+    """Engine clock and socket power while the same launches run, read with
+    `rocm-smi --showmetrics` outside the timed region: ~`seconds` of launches
+    are queued, the tool is sampled once the GPU is busy, then the queue
+    drains.  None when the tool or its fields are unavailable."""
+    import re
+    import subprocess
+
+    import torch
+
+    try:
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        one = max(time.perf_counter() - t0, 1e-4)
+        for _ in range(int(seconds / one) + 1):
+            step()
+        time.sleep(min(0.3, seconds / 3))
+        out = subprocess.run(["rocm-smi", "--showmetrics"], capture_output=True, text=True,
+                             timeout=20).stdout
+        torch.cuda.synchronize()
+    except (OSError, subprocess.SubprocessError):
+        return None
+    power = re.search(r"current_socket_power \(W\): (\d+)", out)
+    clks = re.search(r"current_gfxclks \(MHz\): \[([0-9, ]+)\]", out)
+    if not clks:
+        return None
+    mhz = [int(x) for x in clks.group(1).split(",")]
+    return {"gfxclk_mhz": round(sum(mhz) / len(mhz)), "gfxclk_mhz_per_xcd": mhz,
+            "socket_power_w": int(power.group(1)) if power else None,
+            "source": "rocm-smi --showmetrics while the same launches run (outside the timed region)"}
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -191,6 +224,13 @@ def main() -> int:
     print(f"[bench] {name}: {ms_per_step:.4f} ms/step, kernel {kernel_ms:.4f} ms, "
           f"{value:.1f} TFLOP/s ({result['pct_peak']}% of {PEAK_FP16_TFLOPS})",
           file=sys.stderr, flush=True)
+    clock = sample_clock_power(step)
+    if clock:
+        # the published peak assumes 2.4 GHz; the same peak at the clock the part ran
+        peak_at_clock = PEAK_FP16_TFLOPS * clock["gfxclk_mhz"] / 2400.0
+        clock["peak_at_clock_tflops"] = round(peak_at_clock, 1)
+        clock["frac_at_clock"] = round(achieved / peak_at_clock, 4)
+    result["clock"] = clock
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(result), flush=True)
