@@ -21,7 +21,15 @@
  *   multiply by V.
  *
  *   Mask rule (same page, section "K/V Tile 遍历与核心计算"): a key j is kept
- *   for query i iff i >= j.
+ *   for query i iff i >= j.  With a query sequence shorter than the key
+ *   sequence (queries that follow past_len earlier positions, e.g. a prefill
+ *   after a cached prefix), query row i sits at position i + past_len and
+ *   keeps key j iff i + past_len >= j: page "TileLang性能分析报告：H100上
+ *   FlashAttention吞吐量达1.2PFlops", section "因果掩码优化" (causal mask
+ *   optimisation).  A row that keeps no key at all (possible only when
+ *   i + past_len < 0, or with no keys) has output 0 -- what the division
+ *   guard of the first page's section "最终输出写回与Q tile 迭代" produces from
+ *   an all-zero accumulator -- and log-sum-exp ln(0) = -inf.
  *
  *   Grouped-query heads (same page, section "初始化与Kernel 入口" and the K/V
  *   loads of "K/V Tile 遍历与核心计算"): head_kv = heads / groups and query
@@ -32,10 +40,10 @@
  *   The page "TileLang 与机器学习训练：反向传播算子优化案例" (backward-pass
  *   case), section on the main backward kernel, consumes it as "lse".
  *
- * Layouts (all contiguous, row-major):
- *   q, o : [B][L][H][D]          (BSHD)
- *   k, v : [B][L][Hkv][D]
- *   lse  : [B][H][L]
+ * Layouts (all contiguous, row-major; Lq query rows, Lk key rows):
+ *   q, o : [B][Lq][H][D]          (BSHD)
+ *   k, v : [B][Lk][Hkv][D]
+ *   lse  : [B][H][Lq]
  * q/k/v are IEEE binary16 bit patterns, decoded exactly to double.
  * o and lse are written in double.
  *
@@ -85,25 +93,28 @@ static double h2d(uint16_t h) { return g_half[h]; }
 
 typedef struct {
     const uint16_t *q, *k, *v;
-    int B, L, H, Hkv, D, causal;
+    int B, Lq, Lk, H, Hkv, D, causal, past_len;
     double scale;
 } problem_t;
 
 static size_t q_index(const problem_t *p, int b, int i, int h, int d)
 {
-    return (((size_t)b * p->L + i) * p->H + h) * p->D + d;
+    return (((size_t)b * p->Lq + i) * p->H + h) * p->D + d;
 }
 
 static size_t kv_index(const problem_t *p, int b, int j, int hk, int d)
 {
-    return (((size_t)b * p->L + j) * p->Hkv + hk) * p->D + d;
+    return (((size_t)b * p->Lk + j) * p->Hkv + hk) * p->D + d;
 }
 
-/* Number of keys query i may attend to: all L keys, or keys 0..i under the
- * causal mask (kept iff i >= j). */
+/* Number of keys query i may attend to; the kept keys are always 0..n-1.
+ * Without the mask: all Lk keys.  Under the causal mask: keys j with
+ * i + past_len >= j, clipped to [0, Lk]. */
 static int visible_keys(const problem_t *p, int i)
 {
-    return p->causal ? i + 1 : p->L;
+    if (!p->causal) return p->Lk;
+    long n = (long)i + p->past_len + 1;
+    return n < 0 ? 0 : (n > p->Lk ? p->Lk : (int)n);
 }
 
 /* One output row, straight from the definition.
@@ -112,14 +123,20 @@ static int visible_keys(const problem_t *p, int i)
  *   w_j  = exp(s_j - m),   Z = sum_j w_j
  *   O_d  = sum_j (w_j / Z) * V[b,j,hk,d]
  *   LSE  = m + ln Z
- * `s` is caller-provided scratch of at least L doubles; on return it holds
- * the probabilities w_j / Z of the visible keys (used by the P export). */
+ * `s` is caller-provided scratch of at least Lk doubles; on return it holds
+ * the probabilities w_j / Z of the visible keys (used by the P export).
+ * A row with no visible key: O = 0, LSE = -inf. */
 static void attention_row(const problem_t *p, int b, int h, int i,
                           double *s, double *o_row, double *lse_out)
 {
     int groups = p->H / p->Hkv;
     int hk = h / groups;
     int n = visible_keys(p, i);
+    if (n == 0) {
+        for (int d = 0; d < p->D; ++d) o_row[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
 
     /* step 1: scaled scores */
     for (int j = 0; j < n; ++j) {
@@ -179,16 +196,16 @@ static void *full_worker(void *arg)
 {
     job_t *job = (job_t *)arg;
     const problem_t *p = job->p;
-    double *s = (double *)malloc(sizeof(double) * (size_t)(p->L > 0 ? p->L : 1));
-    long chunks = (p->L + ROW_CHUNK - 1) / ROW_CHUNK;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(p->Lk > 0 ? p->Lk : 1));
+    long chunks = (p->Lq + ROW_CHUNK - 1) / ROW_CHUNK;
     long it;
     while ((it = take_item(job)) >= 0) {
         long bh = it / chunks, c = it % chunks;
         int b = (int)(bh / p->H), h = (int)(bh % p->H);
-        int i_end = (int)((c + 1) * ROW_CHUNK < p->L ? (c + 1) * ROW_CHUNK : p->L);
+        int i_end = (int)((c + 1) * ROW_CHUNK < p->Lq ? (c + 1) * ROW_CHUNK : p->Lq);
         for (int i = (int)(c * ROW_CHUNK); i < i_end; ++i)
             attention_row(p, b, h, i, s, job->o + q_index(p, b, i, h, 0),
-                          job->lse + ((size_t)b * p->H + h) * p->L + i);
+                          job->lse + ((size_t)b * p->H + h) * p->Lq + i);
     }
     free(s);
     return NULL;
@@ -198,7 +215,7 @@ static void *rows_worker(void *arg)
 {
     job_t *job = (job_t *)arg;
     const problem_t *p = job->p;
-    double *s = (double *)malloc(sizeof(double) * (size_t)(p->L > 0 ? p->L : 1));
+    double *s = (double *)malloc(sizeof(double) * (size_t)(p->Lk > 0 ? p->Lk : 1));
     long it;
     while ((it = take_item(job)) >= 0) {
         const int64_t *r = job->rows + 3 * it;
@@ -230,53 +247,64 @@ static void run_pool(job_t *job, void *(*fn)(void *), int nthreads)
 }
 
 /* Returns 0 on success, -1 on invalid arguments (the oracle checks only what
- * it needs to stay in bounds: H divisible by Hkv, positive sizes). */
-static int check_problem(int B, int L, int H, int Hkv, int D)
+ * it needs to stay in bounds: H divisible by Hkv, non-negative sizes). */
+static int check_problem(int B, int Lq, int Lk, int H, int Hkv, int D)
 {
     pthread_once(&g_half_once, fill_half_table);
-    if (B < 0 || L < 0 || H <= 0 || Hkv <= 0 || D <= 0) return -1;
+    if (B < 0 || Lq < 0 || Lk < 0 || H <= 0 || Hkv <= 0 || D <= 0) return -1;
     if (H % Hkv != 0) return -1;
     return 0;
 }
 
-/* Whole forward: o [B][L][H][D], lse [B][H][L] (lse may be NULL).
- * Work is split over (b, h, 64-row chunk) among `nthreads` POSIX threads
- * (0 = all online cores); each row is computed independently, so the thread
- * count never changes a result. */
-int fa_oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                  double *o, double *lse, int B, int L, int H, int Hkv, int D,
-                  int causal, double scale, int nthreads)
+/* Whole forward with Lq query rows and Lk key rows; query row i sits at
+ * position i + past_len under the causal mask (past_len is ignored without
+ * it).  o [B][Lq][H][D], lse [B][H][Lq] (lse may be NULL).  Work is split
+ * over (b, h, 64-row chunk) among `nthreads` POSIX threads (0 = all online
+ * cores); each row is computed independently, so the thread count never
+ * changes a result. */
+int fa_oracle_fwd_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     double *o, double *lse, int B, int Lq, int Lk, int H, int Hkv, int D,
+                     int causal, int past_len, double scale, int nthreads)
 {
-    if (check_problem(B, L, H, Hkv, D)) return -1;
-    problem_t p = {q, k, v, B, L, H, Hkv, D, causal ? 1 : 0, scale};
+    if (check_problem(B, Lq, Lk, H, Hkv, D)) return -1;
+    problem_t p = {q, k, v, B, Lq, Lk, H, Hkv, D, causal ? 1 : 0, past_len, scale};
     double *lse_buf = lse;
-    if (!lse_buf) lse_buf = (double *)malloc(sizeof(double) * ((size_t)B * H * L + 1));
+    if (!lse_buf) lse_buf = (double *)malloc(sizeof(double) * ((size_t)B * H * Lq + 1));
     job_t job;
     memset(&job, 0, sizeof(job));
     job.p = &p;
     job.o = o;
     job.lse = lse_buf;
-    job.n_items = (long)B * H * ((L + ROW_CHUNK - 1) / ROW_CHUNK);
+    job.n_items = (long)B * H * ((Lq + ROW_CHUNK - 1) / ROW_CHUNK);
     if (job.n_items > 0) run_pool(&job, full_worker, nthreads);
     if (!lse) free(lse_buf);
     return 0;
 }
 
-/* Selected rows only: rows holds n_rows triples (b, h, i); o_rows is
- * [n_rows][D], lse_rows is [n_rows].  Same arithmetic as fa_oracle_fwd, so a
- * sampled row equals the corresponding full-forward row bit for bit. */
-int fa_oracle_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                   int B, int L, int H, int Hkv, int D, int causal, double scale,
-                   const int64_t *rows, long n_rows, double *o_rows,
-                   double *lse_rows, int nthreads)
+/* Whole forward with one sequence length L for queries and keys (the
+ * i >= j mask): o [B][L][H][D], lse [B][H][L] (lse may be NULL). */
+int fa_oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  double *o, double *lse, int B, int L, int H, int Hkv, int D,
+                  int causal, double scale, int nthreads)
 {
-    if (check_problem(B, L, H, Hkv, D)) return -1;
+    return fa_oracle_fwd_kv(q, k, v, o, lse, B, L, L, H, Hkv, D, causal, 0, scale, nthreads);
+}
+
+/* Selected rows only: rows holds n_rows triples (b, h, i); o_rows is
+ * [n_rows][D], lse_rows is [n_rows].  Same arithmetic as the whole forward,
+ * so a sampled row equals the corresponding full-forward row bit for bit. */
+int fa_oracle_rows_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      int B, int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len,
+                      double scale, const int64_t *rows, long n_rows, double *o_rows,
+                      double *lse_rows, int nthreads)
+{
+    if (check_problem(B, Lq, Lk, H, Hkv, D)) return -1;
     for (long r = 0; r < n_rows; ++r) {
         const int64_t *t = rows + 3 * r;
-        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= L)
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= Lq)
             return -1;
     }
-    problem_t p = {q, k, v, B, L, H, Hkv, D, causal ? 1 : 0, scale};
+    problem_t p = {q, k, v, B, Lq, Lk, H, Hkv, D, causal ? 1 : 0, past_len, scale};
     job_t job;
     memset(&job, 0, sizeof(job));
     job.p = &p;
@@ -288,22 +316,39 @@ int fa_oracle_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     return 0;
 }
 
-/* Softmax probabilities of one row: probs[j] for j < L, zero for masked keys.
- * Exposed so tests can check that each row of the softmax sums to one. */
-int fa_oracle_row_probs(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                        int B, int L, int H, int Hkv, int D, int causal,
-                        double scale, int b, int h, int i, double *probs)
+int fa_oracle_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   int B, int L, int H, int Hkv, int D, int causal, double scale,
+                   const int64_t *rows, long n_rows, double *o_rows,
+                   double *lse_rows, int nthreads)
 {
-    if (check_problem(B, L, H, Hkv, D)) return -1;
-    if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= L) return -1;
-    problem_t p = {q, k, v, B, L, H, Hkv, D, causal ? 1 : 0, scale};
-    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    return fa_oracle_rows_kv(q, k, v, B, L, L, H, Hkv, D, causal, 0, scale, rows, n_rows, o_rows,
+                             lse_rows, nthreads);
+}
+
+/* Softmax probabilities of one row: probs[j] for j < Lk, zero for masked keys
+ * (all zero for a row with no visible key).  Exposed so tests can check that
+ * each row of the softmax sums to one. */
+int fa_oracle_row_probs_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           int B, int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len,
+                           double scale, int b, int h, int i, double *probs)
+{
+    if (check_problem(B, Lq, Lk, H, Hkv, D)) return -1;
+    if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Lq) return -1;
+    problem_t p = {q, k, v, B, Lq, Lk, H, Hkv, D, causal ? 1 : 0, past_len, scale};
+    double *s = (double *)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
     double *o_row = (double *)malloc(sizeof(double) * (size_t)D);
     double lse;
     attention_row(&p, b, h, i, s, o_row, &lse);
     int n = visible_keys(&p, i);
-    for (int j = 0; j < L; ++j) probs[j] = j < n ? s[j] : 0.0;
+    for (int j = 0; j < Lk; ++j) probs[j] = j < n ? s[j] : 0.0;
     free(s);
     free(o_row);
     return 0;
+}
+
+int fa_oracle_row_probs(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int B, int L, int H, int Hkv, int D, int causal,
+                        double scale, int b, int h, int i, double *probs)
+{
+    return fa_oracle_row_probs_kv(q, k, v, B, L, L, H, Hkv, D, causal, 0, scale, b, h, i, probs);
 }

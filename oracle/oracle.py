@@ -51,6 +51,15 @@ def _bind(path: str):
     lib.fa_oracle_row_probs.argtypes = ([u16p, u16p, u16p] + [c_int] * 6 +
                                        [c_double, c_int, c_int, c_int, f64p])
     lib.fa_oracle_row_probs.restype = c_int
+    lib.fa_oracle_fwd_kv.argtypes = ([u16p, u16p, u16p, f64p, f64p] + [c_int] * 8 +
+                                     [c_double, c_int])
+    lib.fa_oracle_fwd_kv.restype = c_int
+    lib.fa_oracle_rows_kv.argtypes = ([u16p, u16p, u16p] + [c_int] * 8 +
+                                      [c_double, i64p, c_long, f64p, f64p, c_int])
+    lib.fa_oracle_rows_kv.restype = c_int
+    lib.fa_oracle_row_probs_kv.argtypes = ([u16p, u16p, u16p] + [c_int] * 8 +
+                                           [c_double, c_int, c_int, c_int, f64p])
+    lib.fa_oracle_row_probs_kv.restype = c_int
     return lib
 
 
@@ -82,16 +91,24 @@ def _as_half_bits(x) -> np.ndarray:
 
 
 def _shape(q, k, v):
+    """q [B, Lq, H, D], k and v [B, Lk, Hkv, D] (Lq and Lk may differ)."""
     q, k, v = _as_half_bits(q), _as_half_bits(k), _as_half_bits(v)
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D BSHD")
-    B, L, H, D = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != L or k.shape[3] != D:
+    B, Lq, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
-    Hkv = k.shape[2]
+    Lk, Hkv = k.shape[1], k.shape[2]
     if Hkv <= 0 or H % Hkv:
         raise ValueError(f"H={H} is not a multiple of Hkv={Hkv}")
-    return q, k, v, B, L, H, Hkv, D
+    return q, k, v, B, Lq, Lk, H, Hkv, D
+
+
+def default_past_len(Lq: int, Lk: int) -> int:
+    """Position of query row 0 in the key sequence when none is given: the
+    queries are the last Lq positions of the Lk keys (a prefill after a
+    cached prefix), so past_len = Lk - Lq; 0 when the lengths are equal."""
+    return Lk - Lq
 
 
 def _ptr(a, ctype):
@@ -105,54 +122,66 @@ def default_scale(D: int) -> float:
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, nthreads: int = 0,
-            lib=None):
-    """Full attention forward in fp64. Returns (o [B,L,H,D], lse [B,H,L]).
-    ``lib`` selects another build of the same source (used by the tests that
-    check the pins reject deliberately broken copies of the oracle)."""
+            lib=None, past_len: int | None = None):
+    """Full attention forward in fp64. Returns (o [B,Lq,H,D], lse [B,H,Lq]).
+    Under the causal mask query row i sits at position i + past_len of the
+    keys (default Lk - Lq).  ``lib`` selects another build of the same source
+    (used by the tests that check the pins reject deliberately broken copies
+    of the oracle)."""
     lib = lib or _load()
-    q, k, v, B, L, H, Hkv, D = _shape(q, k, v)
+    q, k, v, B, Lq, Lk, H, Hkv, D = _shape(q, k, v)
     scale = default_scale(D) if scale is None else float(scale)
-    o = np.empty((B, L, H, D), np.float64)
-    lse = np.empty((B, H, L), np.float64)
-    rc = lib.fa_oracle_fwd(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-                           _ptr(v, ctypes.c_uint16), _ptr(o, ctypes.c_double),
-                           _ptr(lse, ctypes.c_double), B, L, H, Hkv, D, int(bool(causal)),
-                           scale, int(nthreads))
+    past = default_past_len(Lq, Lk) if past_len is None else int(past_len)
+    o = np.empty((B, Lq, H, D), np.float64)
+    lse = np.empty((B, H, Lq), np.float64)
+    if Lq == Lk and past == 0:
+        rc = lib.fa_oracle_fwd(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                               _ptr(v, ctypes.c_uint16), _ptr(o, ctypes.c_double),
+                               _ptr(lse, ctypes.c_double), B, Lq, H, Hkv, D, int(bool(causal)),
+                               scale, int(nthreads))
+    else:
+        rc = lib.fa_oracle_fwd_kv(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                  _ptr(v, ctypes.c_uint16), _ptr(o, ctypes.c_double),
+                                  _ptr(lse, ctypes.c_double), B, Lq, Lk, H, Hkv, D,
+                                  int(bool(causal)), past, scale, int(nthreads))
     if rc:
         raise ValueError("oracle rejected the problem")
     return o, lse
 
 
 def rows(q, k, v, row_ids, causal: bool = False, scale: float | None = None, nthreads: int = 0,
-         lib=None):
+         lib=None, past_len: int | None = None):
     """Selected rows: row_ids is an int array of (b, h, i) triples, shape [n, 3].
     Returns (o_rows [n, D], lse_rows [n])."""
     lib = lib or _load()
-    q, k, v, B, L, H, Hkv, D = _shape(q, k, v)
+    q, k, v, B, Lq, Lk, H, Hkv, D = _shape(q, k, v)
     scale = default_scale(D) if scale is None else float(scale)
+    past = default_past_len(Lq, Lk) if past_len is None else int(past_len)
     r = np.ascontiguousarray(np.asarray(row_ids, dtype=np.int64).reshape(-1, 3))
     n = r.shape[0]
     o = np.empty((n, D), np.float64)
     lse = np.empty((n,), np.float64)
-    rc = lib.fa_oracle_rows(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-                            _ptr(v, ctypes.c_uint16), B, L, H, Hkv, D, int(bool(causal)), scale,
-                            _ptr(r, ctypes.c_int64), n, _ptr(o, ctypes.c_double),
-                            _ptr(lse, ctypes.c_double), int(nthreads))
+    rc = lib.fa_oracle_rows_kv(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                               _ptr(v, ctypes.c_uint16), B, Lq, Lk, H, Hkv, D, int(bool(causal)),
+                               past, scale, _ptr(r, ctypes.c_int64), n, _ptr(o, ctypes.c_double),
+                               _ptr(lse, ctypes.c_double), int(nthreads))
     if rc:
         raise ValueError("oracle rejected the rows")
     return o, lse
 
 
 def row_probs(q, k, v, b: int, h: int, i: int, causal: bool = False, scale: float | None = None,
-              lib=None):
-    """Softmax probabilities of row (b, h, i) over all L keys (0 where masked)."""
+              lib=None, past_len: int | None = None):
+    """Softmax probabilities of row (b, h, i) over all Lk keys (0 where masked)."""
     lib = lib or _load()
-    q, k, v, B, L, H, Hkv, D = _shape(q, k, v)
+    q, k, v, B, Lq, Lk, H, Hkv, D = _shape(q, k, v)
     scale = default_scale(D) if scale is None else float(scale)
-    p = np.empty((L,), np.float64)
-    rc = lib.fa_oracle_row_probs(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-                                 _ptr(v, ctypes.c_uint16), B, L, H, Hkv, D, int(bool(causal)),
-                                 scale, b, h, i, _ptr(p, ctypes.c_double))
+    past = default_past_len(Lq, Lk) if past_len is None else int(past_len)
+    p = np.empty((Lk,), np.float64)
+    rc = lib.fa_oracle_row_probs_kv(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                    _ptr(v, ctypes.c_uint16), B, Lq, Lk, H, Hkv, D,
+                                    int(bool(causal)), past, scale, b, h, i,
+                                    _ptr(p, ctypes.c_double))
     if rc:
         raise ValueError("oracle rejected the row")
     return p

@@ -19,6 +19,13 @@ log-sum-exp, ...), must each fail at least one pin.  What pins what:
 * small cases            -- L = 1 gives V and s_00; L = 2 is a two-way sigmoid mix
 * invariances            -- key permutation (non-causal), per-row logit shift,
                             per-(b, h) slicing, thread count, the row API
+* Lq != Lk, past_len     -- torch's attention with an explicit boolean mask
+                            (keep j iff i + past_len >= j); Q = 0 gives the mean
+                            of the visible V rows and ln(count); rows that see no
+                            key give O = 0 and LSE = -inf; past_len >= Lk - 1
+                            equals the unmasked result; the queries of a prefill
+                            after a cached prefix equal the last rows of causal
+                            self-attention over the whole sequence
 """
 from __future__ import annotations
 
@@ -239,9 +246,88 @@ def pin_threads_and_rows(lib):
             assert np.array_equal(orow[n], o1[b, i, h]) and lrow[n] == l1[b, h, i]
 
 
+def visible_counts(Lq, Lk, causal, past_len):
+    """Keys query row i keeps: all Lk, or those with i + past_len >= j."""
+    if not causal:
+        return np.full(Lq, Lk)
+    return np.clip(np.arange(Lq) + past_len + 1, 0, Lk)
+
+
+KV_CASES = [
+    # B, Lq, Lk, H, Hkv, D, past_len (None = Lk - Lq)
+    (1, 5, 19, 2, 1, 64, None),
+    (2, 17, 40, 4, 2, 64, None),
+    (1, 33, 33, 2, 2, 16, 7),      # queries shifted forward
+    (1, 30, 12, 2, 1, 64, None),   # more queries than keys: early rows see nothing
+    (2, 9, 25, 4, 4, 8, -4),       # negative offset: first 4 rows see nothing
+    (1, 6, 20, 2, 2, 32, 100),     # offset past the end: every key visible
+]
+
+
+def pin_sdpa_kv(lib):
+    for n, (B, Lq, Lk, H, Hkv, D, past) in enumerate(KV_CASES):
+        q, _, _ = make_qkv(B, Lq, H, Hkv, D, seed=200 + n)
+        _, k, v = make_qkv(B, Lk, H, Hkv, D, seed=300 + n)
+        pl = Lk - Lq if past is None else past
+        scale = 1.0 / math.sqrt(D)
+        for causal in (False, True):
+            o, lse = oracle.forward(q, k, v, causal=causal, past_len=past, lib=lib)
+            keep = torch.ones(Lq, Lk, dtype=torch.bool)
+            if causal:
+                keep = torch.arange(Lq)[:, None] + pl >= torch.arange(Lk)[None, :]
+            qt = q.to(torch.float64).permute(0, 2, 1, 3)
+            kt = k.to(torch.float64).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1)
+            vt = v.to(torch.float64).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1)
+            o_ref = torch.nn.functional.scaled_dot_product_attention(
+                qt, kt, vt, attn_mask=keep, scale=scale).permute(0, 2, 1, 3).numpy()
+            s = (torch.matmul(qt, kt.transpose(-1, -2)) * scale).masked_fill(~keep, float("-inf"))
+            lse_ref = torch.logsumexp(s, dim=-1).numpy()
+            seen = visible_counts(Lq, Lk, causal, pl) > 0
+            assert np.max(np.abs(o[:, seen] - o_ref[:, seen]), initial=0) <= 1e-12, (n, causal)
+            assert np.max(np.abs(lse[:, :, seen] - lse_ref[:, :, seen]), initial=0) <= 1e-12
+            assert np.all(o[:, ~seen] == 0.0), (n, causal)
+            assert np.all(lse[:, :, ~seen] == -np.inf), (n, causal)
+
+
+def pin_zero_q_kv(lib):
+    B, Lq, Lk, H, D = 1, 12, 20, 2, 32
+    _, k, v = make_qkv(B, Lk, H, H, D, seed=400)
+    q = torch.zeros(B, Lq, H, D, dtype=torch.float16)
+    vd = f64(v)
+    for past in (Lk - Lq, -3, 0):
+        o, lse = oracle.forward(q, k, v, causal=True, past_len=past, lib=lib)
+        for i, n in enumerate(visible_counts(Lq, Lk, True, past)):
+            if n == 0:
+                assert np.all(o[0, i] == 0.0) and np.all(lse[0, :, i] == -np.inf)
+            else:
+                assert np.max(np.abs(o[0, i] - vd[0, :n].mean(axis=0))) <= TOL
+                assert np.max(np.abs(lse[0, :, i] - math.log(n))) <= TOL
+
+
+def pin_past_beyond_end_is_unmasked(lib):
+    q, _, _ = make_qkv(1, 10, 2, 1, 64, seed=401)
+    _, k, v = make_qkv(1, 23, 2, 1, 64, seed=402)
+    o1, l1 = oracle.forward(q, k, v, causal=False, lib=lib)
+    for past in (22, 40):
+        o2, l2 = oracle.forward(q, k, v, causal=True, past_len=past, lib=lib)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def pin_prefill_after_prefix(lib):
+    """The last Lq query rows of causal self-attention over Lk positions equal
+    a causal forward of just those rows, placed at past_len = Lk - Lq."""
+    q, k, v = make_qkv(2, 41, 4, 2, 64, seed=403)
+    o_full, l_full = oracle.forward(q, k, v, causal=True, lib=lib)
+    for Lq in (1, 13, 41):
+        qs = q[:, 41 - Lq:].contiguous()
+        o, lse = oracle.forward(qs, k, v, causal=True, lib=lib)  # default past_len = Lk - Lq
+        assert np.array_equal(o, o_full[:, 41 - Lq:]) and np.array_equal(lse, l_full[:, :, 41 - Lq:])
+
+
 PINS = [pin_decoder, pin_sdpa, pin_rows_sum_to_one, pin_constant_v, pin_causal_row0, pin_zero_q,
         pin_one_hot_selection, pin_gqa_equals_repeated_mha, pin_small_L, pin_key_permutation,
-        pin_logit_shift, pin_slices, pin_threads_and_rows]
+        pin_logit_shift, pin_slices, pin_threads_and_rows, pin_sdpa_kv, pin_zero_q_kv,
+        pin_past_beyond_end_is_unmasked, pin_prefill_after_prefix]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -254,10 +340,16 @@ def test_oracle_pin(pin):
 MUTANTS = {
     "scale dropped": ("s[j] = p->scale * dot;", "s[j] = dot;"),
     "kv head h mod Hkv": ("int hk = h / groups;", "int hk = h % p->Hkv;"),
-    "mask admits one future key": ("return p->causal ? i + 1 : p->L;",
-                                   "return p->causal ? (i + 2 < p->L ? i + 2 : p->L) : p->L;"),
-    "mask drops the diagonal": ("return p->causal ? i + 1 : p->L;",
-                                "return p->causal ? (i > 0 ? i : 1) : p->L;"),
+    "mask admits one future key": ("long n = (long)i + p->past_len + 1;",
+                                   "long n = (long)i + p->past_len + 2;"),
+    "mask drops the diagonal": ("long n = (long)i + p->past_len + 1;",
+                                "long n = (long)i + p->past_len;"),
+    "past_len ignored": ("long n = (long)i + p->past_len + 1;", "long n = (long)i + 1;"),
+    "past_len sign flipped": ("long n = (long)i + p->past_len + 1;",
+                              "long n = (long)i - p->past_len + 1;"),
+    "key rows indexed with the query length": (
+        "return (((size_t)b * p->Lk + j) * p->Hkv + hk) * p->D + d;",
+        "return (((size_t)b * p->Lq + j) * p->Hkv + hk) * p->D + d;"),
     "K used in place of V": ("acc += s[j] * h2d(p->v[kv_index(p, b, j, hk, d)]);",
                              "acc += s[j] * h2d(p->k[kv_index(p, b, j, hk, d)]);"),
     "no normalisation": ("s[j] = s[j] / z;", "s[j] = s[j] / (double)n;"),
@@ -268,8 +360,8 @@ MUTANTS = {
     "subnormal exponent": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     "exponent bias": ("ldexp(1.0 + (double)frac / 1024.0, e - 15)",
                       "ldexp(1.0 + (double)frac / 1024.0, e - 14)"),
-    "query row transposed with head": ("return (((size_t)b * p->L + i) * p->H + h) * p->D + d;",
-                                       "return (((size_t)b * p->H + h) * p->L + i) * p->D + d;"),
+    "query row transposed with head": ("return (((size_t)b * p->Lq + i) * p->H + h) * p->D + d;",
+                                       "return (((size_t)b * p->H + h) * p->Lq + i) * p->D + d;"),
 }
 
 
@@ -282,7 +374,8 @@ def test_pins_reject_planted_mistake(name, tmp_path):
     failed = []
     for pin in PINS:
         try:
-            pin(lib)
+            with np.errstate(invalid="ignore"):  # a broken copy may produce inf - inf
+                pin(lib)
         except (AssertionError, ValueError):
             failed.append(pin.__name__)
     assert failed, f"no pin rejects the planted mistake '{name}'"
