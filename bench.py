@@ -8,7 +8,9 @@ the workload's seeded synthetic inputs, already resident in HBM.  Prints one
 JSON line on stdout; extra detail goes to stderr.
 
 Default workload: B=8, H=32, L=4096, D=128, non-causal -- the shape the
-throughput target is quoted on.  FLOPs = 4*B*H*L^2*D (halved when causal).
+throughput target is quoted on.  FLOPs = 4*B*H*L^2*D (halved when causal);
+for queries after cached keys, 4*B*H*D per visible (query, key) pair with the
+diagonal square counted half.
 """
 from __future__ import annotations
 
@@ -106,17 +108,17 @@ def cpu_baseline(w, q, k, v, target_s: float):
 
     def flops(ids):
         if not w.causal:
-            return 4.0 * w.L * w.D * len(ids)
-        return float(sum(4.0 * (int(i) + 1) * w.D for i in ids[:, 2]))
+            return 4.0 * w.keys * w.D * len(ids)
+        return float(sum(4.0 * min(w.keys, int(i) + w.past_len + 1) * w.D for i in ids[:, 2]))
 
     ids = row_ids(threads * 8)
     t0 = time.perf_counter()
-    oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads)
+    oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads, past_len=w.past_len)
     probe = time.perf_counter() - t0
     n = int(max(threads, min(2_000_000, len(ids) * target_s / max(probe, 1e-6))))
     ids = row_ids(n)
     t0 = time.perf_counter()
-    oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads)
+    oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads, past_len=w.past_len)
     dt = time.perf_counter() - t0
     return {"value": flops(ids) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
@@ -170,7 +172,7 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, past_len=w.past_len)
 
     for _ in range(args.warmup):
         step()
@@ -212,7 +214,8 @@ def main() -> int:
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "L": w.L, "D": w.D,
-                   "causal": w.causal, "layout": "BSHD", "seed": args.seed},
+                   "causal": w.causal, "layout": "BSHD", "seed": args.seed,
+                   **({"Lk": w.keys, "past_len": w.past_len} if w.keys != w.L else {})},
         "pct_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),

@@ -39,7 +39,8 @@ typedef struct ihipStream_t *hipStream_t;
 enum fa_status {
     FA_OK = 0,
     FA_ERR_NULLPTR = 1,  /* q, k, v or o is NULL                                  */
-    FA_ERR_SHAPE = 2,    /* B, L, H, Hkv or D negative, or a size overflows int64  */
+    FA_ERR_SHAPE = 2,    /* a size is negative or overflows int64; fa_fwd_kv also:
+                            Lq or Lk > 2^30, or |past_len| > 2^30              */
     FA_ERR_GQA = 3,      /* Hkv <= 0, H <= 0, or H not a multiple of Hkv           */
     FA_ERR_HEADDIM = 4,  /* D is not 64 or 128                                     */
     FA_ERR_SCALE = 5,    /* scale is not finite or not > 0                         */
@@ -81,10 +82,41 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *l
            int B, int L, int H, int Hkv, int D, int causal, float scale,
            hipStream_t stream);
 
+/*
+ * fa_fwd_kv -- attention forward pass with Lq query rows and Lk key rows, for
+ * queries that follow past_len earlier positions of the key sequence (a
+ * prefill after a cached prefix: past_len = Lk - Lq).
+ *
+ * Mask (page "TileLang性能分析报告：H100上FlashAttention吞吐量达1.2PFlops",
+ * section "因果掩码优化"): query row i sits at position i + past_len, and with
+ * causal != 0 it sees key j iff j <= i + past_len.  Without the mask every
+ * query sees all Lk keys and past_len is ignored.  A row that sees no key
+ * (i + past_len < 0, or Lk == 0) gets O = 0 -- the division guard of the
+ * output stage applied to an empty sum -- and LSE = -inf.
+ *
+ * q    device pointer, fp16, contiguous [B][Lq][H][D]                  (read)
+ * k    device pointer, fp16, contiguous [B][Lk][Hkv][D]                (read)
+ * v    device pointer, fp16, contiguous [B][Lk][Hkv][D]                (read)
+ *      k and v may be NULL when Lk == 0.
+ * o    device pointer, fp16, contiguous [B][Lq][H][D]                  (written)
+ * lse  device pointer, fp32, contiguous [B][H][Lq], or NULL            (written)
+ * B, Lq, Lk, H, Hkv, D   as for fa_fwd, with Lq, Lk <= 2^30.
+ * causal, past_len       see above; |past_len| <= 2^30.
+ * scale, stream          as for fa_fwd.
+ *
+ * Ownership, aliasing and error behaviour are those of fa_fwd;
+ * fa_fwd(..., L, ...) is fa_fwd_kv(..., L, L, ..., past_len = 0, ...).
+ * B == 0 or Lq == 0 returns FA_OK and launches nothing.
+ */
+FA_API int fa_fwd_kv(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len,
+              float scale, hipStream_t stream);
+
 /* Human-readable name of an fa_status value (static storage, never NULL). */
 FA_API const char *fa_status_string(int status);
 
-/* Version of this ABI (bumped when a signature or a layout changes). */
+/* Version of this ABI (bumped when an entry point is added or a signature or
+ * a layout changes): 2 = fa_fwd, fa_fwd_kv. */
 FA_API int fa_abi_version(void);
 
 #ifdef __cplusplus

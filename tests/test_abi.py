@@ -35,7 +35,7 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = fa.library()
     names = declared_symbols()
-    assert set(names) == {"fa_fwd", "fa_status_string", "fa_abi_version"}
+    assert set(names) == {"fa_fwd", "fa_fwd_kv", "fa_status_string", "fa_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], check=True,
                          stdout=subprocess.PIPE, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -44,7 +44,7 @@ def test_library_loads_and_exports_header_symbols():
         assert hasattr(lib, n)
     # nothing beyond the declared C ABI leaks out of the library
     assert exported == set(names)
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
 
 
 def test_status_strings():
@@ -90,3 +90,89 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         fa.library()
+
+
+KV_ARGS = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=1, Lq=64, Lk=192, H=2, Hkv=2, D=64, causal=1,
+               past_len=128, scale=0.125, stream=None)
+
+
+def call_kv(**kw):
+    a = dict(KV_ARGS)
+    a.update(kw)
+    return fa.fa_fwd_kv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                        a["H"], a["Hkv"], a["D"], a["causal"], a["past_len"], a["scale"],
+                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(k=None), 1), (dict(v=None), 1),
+    (dict(Lq=-1), 2), (dict(Lk=-1), 2), (dict(Lq=(1 << 30) + 1), 2), (dict(Lk=(1 << 30) + 1), 2),
+    (dict(past_len=(1 << 30) + 1), 2), (dict(past_len=-(1 << 30) - 1), 2),
+    (dict(H=3, Hkv=2), 3), (dict(D=96), 4), (dict(scale=0.0), 5),
+    (dict(k=K + 8), 6), (dict(lse=LSE + 1), 6),
+    # o (Lq rows) overlapping the longer k/v (Lk rows), and k's range reaching o
+    (dict(o=K + 64 * 2 * 64 * 2), 7), (dict(k=O - 64 * 2 * 64 * 2), 7),
+])
+def test_kv_invalid_arguments_rejected_without_launch(kw, status):
+    assert call_kv(**kw) == status
+
+
+def test_kv_empty_problems_are_noops():
+    assert call_kv(B=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert call_kv(Lq=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert call_kv(Lq=0, D=96) == 4
+    # past_len is range-checked even where the mask is off
+    assert call_kv(causal=0, past_len=(1 << 31) - 1) == 2
+
+
+def test_binding_routes_unequal_lengths_to_the_kv_entry_point(monkeypatch):
+    """forward() marshals Lq != Lk (or an explicit past_len) to fa_fwd_kv with
+    the default offset Lk - Lq, and equal lengths to fa_fwd; nothing is
+    launched here (the entry points are replaced)."""
+    torch = pytest.importorskip("torch")
+    seen = {}
+
+    class FakeTensor:
+        def __init__(self, shape):
+            self.shape = shape
+            self.dtype = torch.float16
+            self.is_cuda = True
+            self.device = "dev"
+
+        def dim(self):
+            return 4
+
+        def is_contiguous(self):
+            return True
+
+        def data_ptr(self):
+            return 0x1000
+
+    monkeypatch.setattr(fa, "fa_fwd", lambda *a: seen.setdefault("fwd", a) and 0)
+    monkeypatch.setattr(fa, "fa_fwd_kv", lambda *a: seen.setdefault("kv", a) and 0)
+    monkeypatch.setattr(torch, "Tensor", FakeTensor)
+
+    class Dev:
+        def __init__(self, d):
+            pass
+
+        def __enter__(self):
+            return self
+
+        def __exit__(self, *e):
+            return False
+
+    class Stream:
+        cuda_stream = None
+
+    monkeypatch.setattr(torch.cuda, "device", Dev)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda d=None: Stream())
+    q, k = FakeTensor((1, 16, 2, 64)), FakeTensor((1, 48, 2, 64))
+    o = FakeTensor((1, 16, 2, 64))
+    fa.forward(q, k, k, causal=True, out=o, with_lse=False)
+    assert "kv" in seen and "fwd" not in seen
+    args = seen["kv"]
+    assert args[5:13] == (1, 16, 48, 2, 2, 64, True, 32)  # B, Lq, Lk, H, Hkv, D, causal, past_len
+    seen.clear()
+    fa.forward(q, q, q, causal=True, out=o, with_lse=False)
+    assert "fwd" in seen and "kv" not in seen

@@ -112,7 +112,7 @@ def sample_rows(B, H, L, seed, n_random=96):
 
 FULL = ["mha-b8-h32-L1024-d64", "mha-b8-h32-L1024-d64-causal", "mha-b8-h32-L4096-d128",
         "mha-b8-h32-L4096-d128-causal", "gqa-b2-h32-kv8-L8192-d128-causal",
-        "mha-b1-h32-L16384-d128-causal-qk3"]
+        "mha-b1-h32-L16384-d128-causal-qk3", "prefill-b8-h32-q1024-kv4096-d128-causal"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -130,7 +130,7 @@ def test_full_size_sampled(name):
     assert torch.isfinite(o1).all() and torch.isfinite(lse1).all()
     vmin, vmax = vd.min().float(), vd.max().float()
     assert o1.float().min() >= vmin - 1e-2 and o1.float().max() <= vmax + 1e-2
-    if w.causal:  # row 0 sees only key 0: probability exactly 1
+    if w.causal and w.past_len == 0:  # row 0 sees only key 0: probability exactly 1
         g = w.H // w.Hkv
         assert torch.equal(o1[:, 0], vd[:, 0].repeat_interleave(g, dim=1))
     ids = sample_rows(w.B, w.H, w.L, seed=1)
@@ -200,3 +200,41 @@ def test_binding_reports_misaligned_view():
     with pytest.raises(fa.FaError) as e:
         fa.forward(qm, k.cuda(), v.cuda())
     assert e.value.status == 6
+
+
+# ------------------------------------------- query and key lengths differ
+
+KV_CASES = [
+    # B, Lq, Lk, H, Hkv, D, past_len (None = Lk - Lq: the queries end the key sequence)
+    (1, 1, 300, 4, 2, 128, None),     # one query after 299 cached keys
+    (2, 100, 333, 4, 2, 64, None),    # prefill after a cached prefix, ragged sizes
+    (1, 257, 1000, 2, 1, 128, None),
+    (1, 300, 120, 2, 2, 64, None),    # more queries than keys: rows < 180 see no key
+    (2, 200, 200, 4, 4, 128, 37),     # equal lengths, queries shifted forward
+    (1, 129, 64, 2, 1, 128, -20),     # negative offset: the first 20 rows see no key
+    (1, 64, 0, 2, 2, 64, None),       # no keys at all
+    (1, 77, 500, 4, 1, 64, 600),      # offset past the end: every key visible
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", KV_CASES, ids=[f"q{c[1]}-k{c[2]}-d{c[5]}-p{c[6]}" for c in KV_CASES])
+def test_query_and_key_lengths_differ(case, causal):
+    B, Lq, Lk, H, Hkv, D, past = case
+    q, k, v = make_qkv(B, Lq, H, Hkv, D, seed=500 + Lq + Lk, Lk=Lk)
+    o_ref, lse_ref = oracle.forward(q, k, v, causal=causal, past_len=past)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, past_len=past)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    empty = np.isneginf(lse_ref)  # [B, H, Lq] rows that see no key
+    assert np.array_equal(np.isneginf(lse.double().numpy()), empty), "rows with no key differ"
+    rows = np.transpose(empty, (0, 2, 1))  # [B, Lq, H]
+    assert np.all(o.double().numpy()[rows] == 0.0), "a row with no key has nonzero output"
+    seen = ~rows
+    if seen.any():
+        d = np.abs(o.double().numpy()[seen] - o_ref[seen])
+        dl = np.abs(lse.double().numpy()[~empty] - lse_ref[~empty])
+        msg = (f"B{B} Lq{Lq} Lk{Lk} H{H} Hkv{Hkv} D{D} past={past} causal={causal}: "
+               f"max|dO|={d.max():.3e} mean|dO|={d.mean():.3e} max|dLSE|={dl.max():.3e}")
+        print(msg, flush=True)
+        assert d.max() <= MAX_O and d.mean() <= MEAN_O and dl.max() <= MAX_LSE, msg

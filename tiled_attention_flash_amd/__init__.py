@@ -6,10 +6,12 @@ kernels.  PyTorch supplies device memory and the current stream.
 
     o, lse = tiled_attention_flash_amd.forward(q, k, v, causal=False, scale=None)
 
-q ``[B, L, H, D]``, k/v ``[B, L, Hkv, D]``: contiguous fp16 tensors on the
+q ``[B, Lq, H, D]``, k/v ``[B, Lk, Hkv, D]``: contiguous fp16 tensors on the
 current HIP device (BSHD layout), D in {64, 128}, H a multiple of Hkv.
-Returns o ``[B, L, H, D]`` fp16 and lse ``[B, H, L]`` fp32 (natural-log
-log-sum-exp of each row's scaled scores).
+Returns o ``[B, Lq, H, D]`` fp16 and lse ``[B, H, Lq]`` fp32 (natural-log
+log-sum-exp of each row's scaled scores).  With Lq != Lk (or an explicit
+``past_len``) query row i sits at key position i + past_len, default
+Lk - Lq, which the causal mask uses.
 """
 from __future__ import annotations
 
@@ -17,8 +19,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "fa_fwd", "fa_status_string", "library", "library_path", "FaError",
-           "STATUS"]
+__all__ = ["forward", "fa_fwd", "fa_fwd_kv", "fa_status_string", "library", "library_path",
+           "FaError", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa.so")
@@ -53,6 +55,8 @@ def library():
     c_int = ctypes.c_int
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 6 + [ctypes.c_float, vp]
     lib.fa_fwd.restype = c_int
+    lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 8 + [ctypes.c_float, vp]
+    lib.fa_fwd_kv.restype = c_int
     lib.fa_status_string.argtypes = [c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -72,8 +76,14 @@ def fa_fwd(q, k, v, o, lse, B, L, H, Hkv, D, causal, scale, stream) -> int:
                                 int(bool(causal)), float(scale), stream))
 
 
+def fa_fwd_kv(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, stream) -> int:
+    """Direct call of the C entry point for Lq != Lk; status returned unchanged."""
+    return int(library().fa_fwd_kv(q, k, v, o, lse, int(B), int(Lq), int(Lk), int(H), int(Hkv),
+                                   int(D), int(bool(causal)), int(past_len), float(scale), stream))
+
+
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
-            with_lse: bool = True):
+            with_lse: bool = True, past_len: int | None = None):
     """Attention forward on the current stream.  Returns (o, lse); lse is None
     when ``with_lse`` is False and no ``lse`` buffer is given."""
     import torch
@@ -84,7 +94,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         if t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 4-D [B, L, heads, D] tensor")
     B, L, H, D = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != L or k.shape[3] != D:
+    Lk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
@@ -100,11 +111,15 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     elif lse is not None and (lse.shape != (B, H, L) or lse.dtype != torch.float32 or
                               not lse.is_contiguous() or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 [B, H, L] tensor on q's device")
+    past = Lk - L if past_len is None else int(past_len)
+    ptrs = (q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
+            out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = fa_fwd(q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
-                    out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
-                    B, L, H, Hkv, D, causal, scale, stream)
+        if Lk == L and past == 0:
+            st = fa_fwd(*ptrs, B, L, H, Hkv, D, causal, scale, stream)
+        else:
+            st = fa_fwd_kv(*ptrs, B, L, Lk, H, Hkv, D, causal, past, scale, stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out, lse

@@ -83,7 +83,9 @@ struct Args {
     const _Float16 *q, *k, *v;
     _Float16 *o;
     float *lse;
-    int L, H, Hkv, groups, n_qblocks, n_items;
+    int Lq, Lk;    // query rows, key rows
+    int past_len;  // position of query row 0 among the keys (causal mask only)
+    int H, Hkv, groups, n_qblocks, n_items;
     float scale;       // multiplier of Q.K
     float scale_log2;  // scale * log2(e): exp(scale*x) == exp2(scale_log2*x)
 };
@@ -180,24 +182,24 @@ __device__ __forceinline__ void dma16(const char *base, uint32_t off, _Float16 *
 }
 
 // Issue this wave's share of the direct loads of the K (or V) tile that
-// starts at key k0.  A tile reaching past L loads row L-1 in place of the
+// starts at key k0.  A tile reaching past Lk loads row Lk-1 in place of the
 // missing rows (finite data that the mask hides); rows before key 0 (the
 // first K tile starts at key -32) are not loaded and never read.
 template <int D, int W, bool IS_V>
 __device__ __forceinline__ void issue_loads(const LoadOffsets<D, W> &lo, const _Float16 *base,
-                                            int64_t kv_row, int k0, int L, _Float16 *lds)
+                                            int64_t kv_row, int k0, int Lk, _Float16 *lds)
 {
     using G = Geo<D, W>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const char *tile = (const char *)(base + (int64_t)k0 * kv_row);
-    const bool full = k0 + kBN <= L;
+    const bool full = k0 + kBN <= Lk;
 #pragma unroll
     for (int n = 0; n < G::kLoadsPerWave; ++n) {
         const int blk = G::kLoadsPerWave * wave + n;
         if (k0 + G::kRowsPerLoad * blk < 0) continue;  // whole instruction before key 0
         uint32_t off = IS_V ? lo.v[n] : lo.k[n];
         if (!full) {
-            const int over = k0 + load_row<D, W>(n) - (L - 1);  // rows past the end re-read row L-1
+            const int over = k0 + load_row<D, W>(n) - (Lk - 1);  // rows past the end re-read row Lk-1
             if (over > 0) off -= (uint32_t)(2 * over * kv_row);
         }
         dma16(tile, off, lds + 512 * blk);
@@ -265,21 +267,22 @@ struct Kernel {
         return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 
-    // the block at key k0 holds keys past the sequence end or after a query
-    __device__ __forceinline__ static bool needs_mask(int k0, int L, int wq0)
+    // The block at key k0 holds keys past the end of the keys, or (causal)
+    // keys after the position wp0 of the wavefront's first query.
+    __device__ __forceinline__ static bool needs_mask(int k0, int Lk, int wp0)
     {
-        return (k0 + kSB > L) || (CAUSAL && k0 + kSB - 1 > wq0);
+        return (k0 + kSB > Lk) || (CAUSAL && k0 + kSB - 1 > wp0);
     }
 
-    // Mask keys past the sequence end, and keys after the query (causal).
-    // Register r holds key k0 + 4*half + 8(r/4) + r%4, so one per-lane bound
-    // decides every element.
-    __device__ __forceinline__ static void mask(floatx16 &sacc, int k0, int L, int qi)
+    // Mask keys past the end of the keys, and (causal) keys after the query's
+    // position qp (its row plus past_len).  Register r holds key
+    // k0 + 4*half + 8(r/4) + r%4, so one per-lane bound decides every element.
+    __device__ __forceinline__ static void mask(floatx16 &sacc, int k0, int Lk, int qp)
     {
         const int half = (threadIdx.x & 63) >> 5;
-        int bound = L - k0 - 4 * half;  // hide offsets >= bound
+        int bound = Lk - k0 - 4 * half;  // hide offsets >= bound
         if (CAUSAL) {
-            const int cb = qi - k0 - 4 * half + 1;
+            const int cb = qp - k0 - 4 * half + 1;
             bound = cb < bound ? cb : bound;
         }
 #pragma unroll
@@ -336,21 +339,24 @@ struct Kernel {
 
     // Lazy rescale: raise the reference maximum only when some row's block
     // maximum outgrew it by more than 2^kRescaleLog2 (decided for the whole
-    // wavefront); O and l are scaled by the same factor.
+    // wavefront); O and l are scaled by the same factor.  A row that has
+    // seen no key yet keeps m = -inf and uses 0 as its exponent offset, so
+    // its masked scores still give exp2(-inf) = 0 (never -inf - -inf); its
+    // first visible key always takes this branch.
     __device__ __forceinline__ static void rescale(State &st, float mx, float c)
     {
         const bool grow = (mx - st.m) * c > kRescaleLog2;
         if (__builtin_amdgcn_ballot_w64(grow)) {
             const float m_new = fmaxf(st.m, mx);
-            const float sf = exp2_fast((st.m - m_new) * c);
+            const float sf = st.m == m_new ? 1.0f : exp2_fast((st.m - m_new) * c);
             st.l *= sf;
 #pragma unroll
             for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) st.oacc[i][r] *= sf;
             st.m = m_new;
+            st.mc = m_new == -__builtin_huge_valf() ? 0.0f : m_new * c;
         }
-        st.mc = st.m * c;
     }
 
     // P = exp2(S*c - m*c) for score pair p (registers 2p, 2p+1), rounded to
@@ -385,7 +391,7 @@ struct Kernel {
     template <bool NEXT>
     __device__ __forceinline__ static void body(State &st, const floatx16 &sc, floatx16 &sn,
                                                 const _Float16 *kl, const _Float16 *vl,
-                                                bool mask_next, int k0_next, int L, int qi, float c,
+                                                bool mask_next, int k0_next, int Lk, int qp, float c,
                                                 float &mx_next)
     {
         half8 pf[kCS];
@@ -430,7 +436,7 @@ struct Kernel {
             if (n + kVAhead < kN) va[n + kVAhead] = vfrag(st, vl, (n + kVAhead) % kDBlocks, (n + kVAhead) / kDBlocks);
             if (kPairsA + n < kPairs) exp_pair(sc, pf, rs, kPairsA + n, mc, c);
             if constexpr (NEXT) {
-                if (n == kMaxFrom && mask_next) mask(sn, k0_next, L, qi);
+                if (n == kMaxFrom && mask_next) mask(sn, k0_next, Lk, qp);
                 if (n >= kMaxFrom) {
                     constexpr int kSlots = kN - kMaxFrom;
 #pragma unroll
@@ -454,20 +460,20 @@ struct Kernel {
     // every wavefront of the workgroup runs the same straight-line code.
     __device__ __forceinline__ static void block_next(State &st, const floatx16 &sc, floatx16 &sn,
                                                       const _Float16 *kl, const _Float16 *vl, int u,
-                                                      int L, int wq0, int qi, float c)
+                                                      int Lk, int wp0, int qp, float c)
     {
         const int k0n = kSB * (u + 1);
         float mx;
-        body<true>(st, sc, sn, kl, vl, needs_mask(k0n, L, wq0), k0n, L, qi, c, mx);
+        body<true>(st, sc, sn, kl, vl, needs_mask(k0n, Lk, wp0), k0n, Lk, qp, c, mx);
         rescale(st, mx, c);
     }
 
     // the last score block of the work item
     __device__ __forceinline__ static void block_last(State &st, const floatx16 &sc, floatx16 &sn,
-                                                      const _Float16 *vl, int L, int qi, float c)
+                                                      const _Float16 *vl, int Lk, int qp, float c)
     {
         float mx;
-        body<false>(st, sc, sn, nullptr, vl, false, 0, L, qi, c, mx);
+        body<false>(st, sc, sn, nullptr, vl, false, 0, Lk, qp, c, mx);
     }
 
     // LDS tile t (P = t % 2) covers score blocks u = 2t (scores in sa) and
@@ -480,15 +486,15 @@ struct Kernel {
     template <int P>
     __device__ __forceinline__ static void tile_start(const LoadOffsets<D, W> &lo, const _Float16 *kbase,
                                                       const _Float16 *vbase, int64_t kv_row, int t,
-                                                      int n_tiles, int n_blocks, int L,
+                                                      int n_tiles, int n_blocks, int Lk,
                                                       _Float16 (*klds)[G::kTile],
                                                       _Float16 (*vlds)[G::kTile])
     {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K(t), V(t) have landed
         __syncthreads();                // ... and every wave's
         if (2 * t + 3 < n_blocks)
-            issue_loads<D, W, false>(lo, kbase, kv_row, kBN * (t + 1) + kSB, L, klds[P]);
-        if (t + 1 < n_tiles) issue_loads<D, W, true>(lo, vbase, kv_row, kBN * (t + 1), L, vlds[P ^ 1]);
+            issue_loads<D, W, false>(lo, kbase, kv_row, kBN * (t + 1) + kSB, Lk, klds[P]);
+        if (t + 1 < n_tiles) issue_loads<D, W, true>(lo, vbase, kv_row, kBN * (t + 1), Lk, vlds[P ^ 1]);
     }
 
     // a tile whose two blocks both have a successor
@@ -496,14 +502,14 @@ struct Kernel {
     __device__ __forceinline__ static void tile(State &st, floatx16 &sa, floatx16 &sb,
                                                 const LoadOffsets<D, W> &lo, const _Float16 *kbase,
                                                 const _Float16 *vbase, int64_t kv_row, int t,
-                                                int n_tiles, int n_blocks, int L, int wq0, int qi,
+                                                int n_tiles, int n_blocks, int Lk, int wp0, int qp,
                                                 float c, _Float16 (*klds)[G::kTile],
                                                 _Float16 (*vlds)[G::kTile])
     {
-        tile_start<P>(lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, klds, vlds);
+        tile_start<P>(lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, klds, vlds);
         const _Float16 *kl = klds[P ^ 1], *vl = vlds[P];
-        block_next(st, sa, sb, kl, vl, 2 * t, L, wq0, qi, c);
-        block_next(st, sb, sa, kl + kSB * D, vl + kSB * D, 2 * t + 1, L, wq0, qi, c);
+        block_next(st, sa, sb, kl, vl, 2 * t, Lk, wp0, qp, c);
+        block_next(st, sb, sa, kl + kSB * D, vl + kSB * D, 2 * t + 1, Lk, wp0, qp, c);
     }
 
     // the final tile: block 2t+1, if it exists, is the last one
@@ -511,17 +517,17 @@ struct Kernel {
     __device__ __forceinline__ static void tile_final(State &st, floatx16 &sa, floatx16 &sb,
                                                       const LoadOffsets<D, W> &lo, const _Float16 *kbase,
                                                       const _Float16 *vbase, int64_t kv_row, int t,
-                                                      int n_tiles, int n_blocks, int L, int wq0, int qi,
+                                                      int n_tiles, int n_blocks, int Lk, int wp0, int qp,
                                                       float c, _Float16 (*klds)[G::kTile],
                                                       _Float16 (*vlds)[G::kTile])
     {
-        tile_start<P>(lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, klds, vlds);
+        tile_start<P>(lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, klds, vlds);
         const _Float16 *kl = klds[P ^ 1], *vl = vlds[P];
         if (2 * t + 1 < n_blocks) {
-            block_next(st, sa, sb, kl, vl, 2 * t, L, wq0, qi, c);
-            block_last(st, sb, sa, vl + kSB * D, L, qi, c);
+            block_next(st, sa, sb, kl, vl, 2 * t, Lk, wp0, qp, c);
+            block_last(st, sb, sa, vl + kSB * D, Lk, qp, c);
         } else {
-            block_last(st, sa, sb, vl, L, qi, c);
+            block_last(st, sa, sb, vl, Lk, qp, c);
         }
     }
 
@@ -545,83 +551,96 @@ struct Kernel {
         const int hk = rest % a.Hkv;
         const int b = rest / a.Hkv;
         const int h = hk * a.groups + g;
-        const int L = a.L;
+        const int Lq = a.Lq, Lk = a.Lk;
         const int q0 = qb * kBM;
 
         const int64_t q_row = (int64_t)a.H * D, kv_row = (int64_t)a.Hkv * D;
-        const _Float16 *qbase = a.q + (int64_t)b * L * q_row + (int64_t)h * D;
-        const _Float16 *kbase = a.k + (int64_t)b * L * kv_row + (int64_t)hk * D;
-        const _Float16 *vbase = a.v + (int64_t)b * L * kv_row + (int64_t)hk * D;
+        const _Float16 *qbase = a.q + (int64_t)b * Lq * q_row + (int64_t)h * D;
+        const _Float16 *kbase = a.k + (int64_t)b * Lk * kv_row + (int64_t)hk * D;
+        const _Float16 *vbase = a.v + (int64_t)b * Lk * kv_row + (int64_t)hk * D;
 
-        const int kv_end = CAUSAL ? (q0 + kBM < L ? q0 + kBM : L) : L;
-        const int n_blocks = (kv_end + kSB - 1) / kSB;
-        const int n_tiles = (kv_end + kBN - 1) / kBN;
-
-        // K tile -1 (keys 0..31 in its upper half) and V tile 0 in flight
-        // while Q is fetched
-        LoadOffsets<D, W> lo;
-        init_load_offsets<D, W>(lo, kv_row);
-        issue_loads<D, W, false>(lo, kbase, kv_row, -kSB, L, klds[0]);
-        issue_loads<D, W, true>(lo, vbase, kv_row, 0, L, vlds[0]);
+        // keys the work item can see: all of them, or (causal) up to the
+        // position of its last query row
+        int kv_end = Lk;
+        if (CAUSAL) {
+            const int last = (q0 + kBM < Lq ? q0 + kBM : Lq) + a.past_len;
+            kv_end = last < Lk ? last : Lk;
+        }
+        const int n_blocks = kv_end > 0 ? (kv_end + kSB - 1) / kSB : 0;
+        const int n_tiles = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
 
         State st;
         const int wq0 = q0 + 32 * wave;
         const int qi = wq0 + col;
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            half8 val = {};
-            if (qi < L) val = *(const half8 *)(qbase + (int64_t)qi * q_row + 16 * s + 8 * half);
-            st.qf[s] = val;
-        }
+        const int wp0 = wq0 + a.past_len;  // key position of the wavefront's first query
+        const int qp = qi + a.past_len;    // key position of this lane's query
 #pragma unroll
         for (int i = 0; i < kDBlocks; ++i) st.oacc[i] = floatx16{};
         st.m = -__builtin_huge_valf();
+        st.mc = 0.0f;
         st.l = 0.0f;
-        // K: row = col (+ 32 for the upper half of a tile), logical chunk 2s + half
-        st.k_base = col * D + 8 * k_chunk<D>(col, half);
-        // V transpose read: 16-lane group gg = lane/16 (d half gg%2, key half
-        // gg/2), j = lane%16 -> row 4*(gg/2) + j/4 (+ 16*cs [+ 8]),
-        // d = 32*i + 16*(gg%2) + 4*(j%4)
-        {
-            const int gg = lane >> 4, j = lane & 15;
-            const int row = 4 * (gg >> 1) + (j >> 2);
-            const int d = 16 * (gg & 1) + 4 * (j & 3);
-            st.v_base = row * D + 8 * v_chunk<D>(row, d >> 3) + (d & 7);
-        }
-        const float c = a.scale_log2;
 
-        // prologue: scores and reference maximum of block 0 (every wavefront
-        // sees key 0); K tile 0 in flight
-        floatx16 sa, sb;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (n_blocks > 1) issue_loads<D, W, false>(lo, kbase, kv_row, kSB, L, klds[1]);
-        s_product(sa, st, klds[0] + kSB * D);
-        if (needs_mask(0, L, wq0)) mask(sa, 0, L, qi);
-        rescale(st, block_max(sa), c);
+        // a work item that sees no key (every row: O = 0, LSE = -inf) skips
+        // the pipeline; n_blocks is the same for the whole workgroup
+        if (n_blocks > 0) {
+            // K tile -1 (keys 0..31 in its upper half) and V tile 0 in flight
+            // while Q is fetched
+            LoadOffsets<D, W> lo;
+            init_load_offsets<D, W>(lo, kv_row);
+            issue_loads<D, W, false>(lo, kbase, kv_row, -kSB, Lk, klds[0]);
+            issue_loads<D, W, true>(lo, vbase, kv_row, 0, Lk, vlds[0]);
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                half8 val = {};
+                if (qi < Lq) val = *(const half8 *)(qbase + (int64_t)qi * q_row + 16 * s + 8 * half);
+                st.qf[s] = val;
+            }
+            // K: row = col (+ 32 for the upper half of a tile), logical chunk 2s + half
+            st.k_base = col * D + 8 * k_chunk<D>(col, half);
+            // V transpose read: 16-lane group gg = lane/16 (d half gg%2, key
+            // half gg/2), j = lane%16 -> row 4*(gg/2) + j/4 (+ 16*cs [+ 8]),
+            // d = 32*i + 16*(gg%2) + 4*(j%4)
+            {
+                const int gg = lane >> 4, j = lane & 15;
+                const int row = 4 * (gg >> 1) + (j >> 2);
+                const int d = 16 * (gg & 1) + 4 * (j & 3);
+                st.v_base = row * D + 8 * v_chunk<D>(row, d >> 3) + (d & 7);
+            }
+            const float c = a.scale_log2;
 
-        // tiles t < n_main = n_tiles - 1 have a successor for both blocks;
-        // tile n_tiles - 1 holds the last block
-        const int n_main = (n_blocks - 1) / 2;
-        int t = 0;
-        for (; t + 1 < n_main; t += 2) {
-            tile<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
-            tile<1>(st, sa, sb, lo, kbase, vbase, kv_row, t + 1, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
+            // prologue: scores and reference maximum of block 0; K tile 0 in flight
+            floatx16 sa, sb;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (n_blocks > 1) issue_loads<D, W, false>(lo, kbase, kv_row, kSB, Lk, klds[1]);
+            s_product(sa, st, klds[0] + kSB * D);
+            if (needs_mask(0, Lk, wp0)) mask(sa, 0, Lk, qp);
+            rescale(st, block_max(sa), c);
+
+            // tiles t < n_main = n_tiles - 1 have a successor for both blocks;
+            // tile n_tiles - 1 holds the last block
+            const int n_main = (n_blocks - 1) / 2;
+            int t = 0;
+            for (; t + 1 < n_main; t += 2) {
+                tile<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
+                tile<1>(st, sa, sb, lo, kbase, vbase, kv_row, t + 1, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
+            }
+            if (t < n_main) {
+                tile<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
+                ++t;
+            }
+            if (t & 1)
+                tile_final<1>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
+            else
+                tile_final<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
         }
-        if (t < n_main) {
-            tile<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
-            ++t;
-        }
-        if (t & 1)
-            tile_final<1>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
-        else
-            tile_final<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, L, wq0, qi, c, klds, vlds);
 
         // ---- finalise: O = acc / l (guarded as on the page), LSE = scale*m + ln l
+        // (a row that saw no key: acc = 0, l = 0, m = -inf -> O = 0, LSE = -inf)
         const float lt = pair_sum(st.l);
         const float inv = 1.0f / (lt > 1e-6f ? lt : 1.0f);
-        if (qi < L) {
-            _Float16 *orow = a.o + (int64_t)b * L * q_row + (int64_t)qi * q_row + (int64_t)h * D;
+        if (qi < Lq) {
+            _Float16 *orow = a.o + (int64_t)b * Lq * q_row + (int64_t)qi * q_row + (int64_t)h * D;
 #pragma unroll
             for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
@@ -634,7 +653,7 @@ struct Kernel {
                     *(half4 *)(orow + 32 * i + 8 * rb + 4 * half) = out;
                 }
             if (a.lse && half == 0)
-                a.lse[((int64_t)b * a.H + h) * L + qi] = st.m * a.scale + __logf(lt);
+                a.lse[((int64_t)b * a.H + h) * Lq + qi] = st.m * a.scale + __logf(lt);
         }
     }
 };
@@ -652,7 +671,7 @@ int launch(Args args, hipStream_t stream)
 {
     constexpr int W = CAUSAL ? 4 : 8;
     using K = Kernel<D, CAUSAL, W>;
-    args.n_qblocks = (args.L + K::kBM - 1) / K::kBM;
+    args.n_qblocks = (args.Lq + K::kBM - 1) / K::kBM;
     const int64_t items = (int64_t)args.n_items * args.n_qblocks;  // n_items holds B*H here
     if (items > 0x7fffffff) return FA_ERR_SHAPE;
     args.n_items = (int)items;
@@ -675,7 +694,9 @@ int launch_forward(const Problem &p, hipStream_t stream)
     a.v = (const _Float16 *)p.v;
     a.o = (_Float16 *)p.o;
     a.lse = p.lse;
-    a.L = p.L;
+    a.Lq = p.Lq;
+    a.Lk = p.Lk;
+    a.past_len = p.past_len;
     a.H = p.H;
     a.Hkv = p.Hkv;
     a.groups = p.H / p.Hkv;

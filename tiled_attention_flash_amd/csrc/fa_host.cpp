@@ -28,24 +28,27 @@ bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
 
 bool misaligned(const void *p, uintptr_t to) { return ((uintptr_t)p & (to - 1)) != 0; }
 
-}  // namespace
-
-extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
-                      int L, int H, int Hkv, int D, int causal, float scale, hipStream_t stream)
+// Shared validation and dispatch of both entry points.
+int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Lq, int Lk,
+            int H, int Hkv, int D, int causal, int past_len, float scale, hipStream_t stream)
 {
-    if (B < 0 || L < 0 || H < 0 || Hkv < 0 || D < 0) return FA_ERR_SHAPE;
+    if (B < 0 || Lq < 0 || Lk < 0 || H < 0 || Hkv < 0 || D < 0) return FA_ERR_SHAPE;
     if (H <= 0 || Hkv <= 0 || H % Hkv != 0) return FA_ERR_GQA;
     if (D != 64 && D != 128) return FA_ERR_HEADDIM;
     if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
-
-    int64_t q_elems = elems4(B, L, H, D);
-    int64_t kv_elems = elems4(B, L, Hkv, D);
-    int64_t lse_elems = elems4(B, H, L, 1);
-    if (q_elems < 0 || kv_elems < 0 || lse_elems < 0 || q_elems > INT64_MAX / 4)
+    // positions i + past_len and key indices stay far from int overflow
+    if (Lq > (1 << 30) || Lk > (1 << 30) || past_len > (1 << 30) || past_len < -(1 << 30))
         return FA_ERR_SHAPE;
-    if (B == 0 || L == 0) return FA_OK;  // nothing to compute; pointers may be null
 
-    if (!q || !k || !v || !o) return FA_ERR_NULLPTR;
+    int64_t q_elems = elems4(B, Lq, H, D);
+    int64_t kv_elems = elems4(B, Lk, Hkv, D);
+    int64_t lse_elems = elems4(B, H, Lq, 1);
+    if (q_elems < 0 || kv_elems < 0 || lse_elems < 0 || q_elems > INT64_MAX / 4 ||
+        kv_elems > INT64_MAX / 4)
+        return FA_ERR_SHAPE;
+    if (B == 0 || Lq == 0) return FA_OK;  // nothing to compute; pointers may be null
+
+    if (!q || !o || (Lk > 0 && (!k || !v))) return FA_ERR_NULLPTR;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
         misaligned(lse, 4))
         return FA_ERR_ALIGN;
@@ -57,8 +60,23 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
         overlaps(lse, lse_bytes, v, kv_bytes))
         return FA_ERR_ALIAS;
 
-    fa::Problem p{q, k, v, o, lse, B, L, H, Hkv, D, causal != 0, scale};
+    fa::Problem p{q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal != 0, causal ? past_len : 0, scale};
     return fa::launch_forward(p, stream);
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                      int L, int H, int Hkv, int D, int causal, float scale, hipStream_t stream)
+{
+    return forward(q, k, v, o, lse, B, L, L, H, Hkv, D, causal, 0, scale, stream);
+}
+
+extern "C" int fa_fwd_kv(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                         int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len,
+                         float scale, hipStream_t stream)
+{
+    return forward(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, stream);
 }
 
 extern "C" const char *fa_status_string(int status)
@@ -66,7 +84,7 @@ extern "C" const char *fa_status_string(int status)
     switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULLPTR: return "FA_ERR_NULLPTR: q, k, v or o is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative size or size overflow";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative size, size overflow, or |past_len| > 2^30";
     case FA_ERR_GQA: return "FA_ERR_GQA: H and Hkv must be positive and H a multiple of Hkv";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
@@ -78,4 +96,4 @@ extern "C" const char *fa_status_string(int status)
     }
 }
 
-extern "C" int fa_abi_version(void) { return 1; }
+extern "C" int fa_abi_version(void) { return 2; }

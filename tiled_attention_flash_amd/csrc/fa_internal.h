@@ -12,11 +12,12 @@ namespace fa {
 // Validated problem description handed to the launcher.  Sizes fit in int;
 // every element offset derived from them fits in int64.
 struct Problem {
-    const void *q, *k, *v;
+    const void *q, *k, *v;  // k, v may be null when Lk == 0
     void *o;
     float *lse;  // may be null
-    int B, L, H, Hkv, D;
+    int B, Lq, Lk, H, Hkv, D;
     bool causal;
+    int past_len;  // position of query row 0 among the keys (causal only); |past_len| <= 2^30
     float scale;
 };
 

@@ -5,9 +5,10 @@ fp64 oracle consume: it draws the random Q/K/V and nothing else.  It holds none
 of the attention arithmetic.
 
 Recipe (every workload): a CPU ``torch.Generator`` seeded with ``seed`` draws,
-in this order, Q ``[B, L, H, D]``, K ``[B, L, Hkv, D]`` and V ``[B, L, Hkv, D]``
-as i.i.d. N(0, 1) float32; the long-sequence workload then multiplies Q and K
-by 3 in float32 to widen the softmax's logit range; finally all three are
+in this order, Q ``[B, Lq, H, D]``, K ``[B, Lk, Hkv, D]`` and V ``[B, Lk, Hkv, D]``
+as i.i.d. N(0, 1) float32 (Lq = Lk = L unless a workload says otherwise); the
+long-sequence workload then multiplies Q and K by 3 in float32 to widen the
+softmax's logit range; finally all three are
 rounded to float16 (round-to-nearest-even).  The same float16 tensors go to the
 oracle (host) and to the GPU.  Layout is BSHD, contiguous.  The scale is
 1/sqrt(D), the value the TileLang AMD page sets up at kernel entry.
@@ -30,6 +31,20 @@ class Workload:
     D: int
     causal: bool
     qk_mult: float = 1.0  # Q and K are multiplied by this before the fp16 cast
+    Lk: int | None = None  # key rows; None = L (queries and keys equally long)
+
+    @property
+    def Lq(self) -> int:
+        return self.L
+
+    @property
+    def keys(self) -> int:
+        return self.L if self.Lk is None else self.Lk
+
+    @property
+    def past_len(self) -> int:
+        """Key position of query row 0: the queries are the last L of the keys."""
+        return self.keys - self.L
 
     @property
     def scale(self) -> float:
@@ -37,24 +52,24 @@ class Workload:
 
     @property
     def flops(self) -> float:
-        """Attention forward work: two contractions of 2*L*L*D flops per
-        (batch, head), i.e. 4*B*H*L^2*D, counted as exactly half when causal."""
-        f = 4.0 * self.B * self.H * self.L * self.L * self.D
-        return f / 2 if self.causal else f
+        """Attention forward work: two contractions of 2*D flops per (query,
+        key) pair.  Equal lengths: 4*B*H*L^2*D, counted as exactly half when
+        causal.  Queries after past_len cached keys, causal: the rectangle of
+        past keys plus half of the Lq x Lq square."""
+        pairs = float(self.L) * self.keys
+        if self.causal:
+            pairs = float(self.L) * self.past_len + self.L * self.L / 2
+        return 4.0 * self.B * self.H * self.D * pairs
 
     @property
     def algorithmic_bytes(self) -> int:
         """Each tensor moved once: Q and O (fp16), K and V (fp16), LSE (fp32)."""
         qo = 2 * self.B * self.L * self.H * self.D * 2
-        kv = 2 * self.B * self.L * self.Hkv * self.D * 2
+        kv = 2 * self.B * self.keys * self.Hkv * self.D * 2
         return qo + kv + self.B * self.H * self.L * 4
 
-    def with_causal(self, causal: bool) -> "Workload":
-        return Workload(self.name + ("-causal" if causal else "-noncausal"), self.B, self.H,
-                        self.Hkv, self.L, self.D, causal, self.qk_mult)
 
-
-# The five workloads the method is measured on (B, H, Hkv, L, D, causal).
+# The workloads the method is measured on (B, H, Hkv, L, D, causal[, qk_mult, Lk]).
 WORKLOADS = {
     "tiny-mha-L128-d64": Workload("tiny-mha-L128-d64", 1, 2, 2, 128, 64, False),
     "tiny-mha-L128-d64-causal": Workload("tiny-mha-L128-d64-causal", 1, 2, 2, 128, 64, True),
@@ -64,19 +79,24 @@ WORKLOADS = {
     "mha-b8-h32-L4096-d128-causal": Workload("mha-b8-h32-L4096-d128-causal", 8, 32, 32, 4096, 128, True),
     "gqa-b2-h32-kv8-L8192-d128-causal": Workload("gqa-b2-h32-kv8-L8192-d128-causal", 2, 32, 8, 8192, 128, True),
     "mha-b1-h32-L16384-d128-causal-qk3": Workload("mha-b1-h32-L16384-d128-causal-qk3", 1, 32, 32, 16384, 128, True, 3.0),
+    # 1024 new queries after 3072 cached positions (a prefill continuing a prefix)
+    "prefill-b8-h32-q1024-kv4096-d128-causal": Workload(
+        "prefill-b8-h32-q1024-kv4096-d128-causal", 8, 32, 32, 1024, 128, True, 1.0, 4096),
 }
 
 HEADLINE = "mha-b8-h32-L4096-d128"
 
 
 def make_qkv(B: int, L: int, H: int, Hkv: int, D: int, seed: int = 0, qk_mult: float = 1.0,
-             device: str | torch.device = "cpu"):
-    """Seeded fp16 Q, K, V (BSHD, contiguous) following the recipe above."""
+             device: str | torch.device = "cpu", Lk: int | None = None):
+    """Seeded fp16 Q, K, V (BSHD, contiguous) following the recipe above;
+    K and V have Lk rows (default L)."""
+    Lk = L if Lk is None else Lk
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     q = torch.randn((B, L, H, D), generator=g, dtype=torch.float32)
-    k = torch.randn((B, L, Hkv, D), generator=g, dtype=torch.float32)
-    v = torch.randn((B, L, Hkv, D), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Lk, Hkv, D), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Lk, Hkv, D), generator=g, dtype=torch.float32)
     if qk_mult != 1.0:
         q = q * qk_mult
         k = k * qk_mult
@@ -87,4 +107,5 @@ def make_qkv(B: int, L: int, H: int, Hkv: int, D: int, seed: int = 0, qk_mult: f
 
 
 def workload_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu"):
-    return make_qkv(w.B, w.L, w.H, w.Hkv, w.D, seed=seed, qk_mult=w.qk_mult, device=device)
+    return make_qkv(w.B, w.L, w.H, w.Hkv, w.D, seed=seed, qk_mult=w.qk_mult, device=device,
+                    Lk=w.keys)
