@@ -26,13 +26,19 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·L²·D, causal halved) + % of MFMA FP16 peak"
 PEAK_FP16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
-KERNEL_SRC = os.path.join(ROOT, "tiled_attention_flash_amd", "csrc", "fa_fwd_kernel.hip")
+PEAK_HBM_GBS = 8000.0  # HBM3E, published
+CSRC = os.path.join(ROOT, "tiled_attention_flash_amd", "csrc")
+KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("fa_device.h", "fa_fwd_kernel.hip",
+                                                 "fa_splitkv_kernel.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -49,37 +55,101 @@ def measured_traffic(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def sample_clock_power(step, seconds: float = 1.5):
-    """Engine clock and socket power while the same launches run, read with
-    `rocm-smi --showmetrics` outside the timed region: ~`seconds` of launches
-    are queued, the tool is sampled once the GPU is busy, then the queue
-    drains.  None when the tool or its fields are unavailable."""
-    import re
-    import subprocess
+def _device_sysfs(dev_index: int = 0):
+    """The sysfs directory (`/sys/class/drm/cardN/device`) of the HIP device,
+    found through its PCI address; None when it is not visible."""
+    import glob
 
     import torch
 
+    props = torch.cuda.get_device_properties(dev_index)
     try:
-        t0 = time.perf_counter()
+        addr = "%04x:%02x:%02x" % (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+    except AttributeError:
+        addr = None
+    cands = []
+    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        pci = os.path.basename(os.path.realpath(d))
+        cands.append((pci, d))
+    for pci, d in cands:
+        if addr and pci.startswith(addr):
+            return d
+    return cands[0][1] if len(cands) == 1 else None
+
+
+def _read(path):
+    try:
+        with open(path) as f:
+            return f.read()
+    except OSError:
+        return None
+
+
+def _power_w(dev):
+    import glob
+
+    for name in ("power1_average", "power1_input"):
+        for p in glob.glob(os.path.join(dev, "hwmon", "hwmon*", name)):
+            t = _read(p)
+            if t and t.strip().isdigit() and int(t) > 0:
+                return int(t) / 1e6
+    return None
+
+
+def _sclk_mhz(dev):
+    """Current engine clock: the starred level of pp_dpm_sclk ("1: 2100Mhz *")."""
+    import re
+
+    t = _read(os.path.join(dev, "pp_dpm_sclk"))
+    if not t:
+        return None
+    for line in t.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+            if m:
+                return int(m.group(1))
+    return None
+
+
+def sample_clock_power(step, seconds: float = 1.5, samples: int = 8):
+    """Engine clock and board power while the same launches run, outside the
+    timed region: about `seconds` of launches are queued, then the device's
+    sysfs files (`pp_dpm_sclk`, hwmon `power1_average` or `power1_input`) are
+    read `samples` times while they drain -- plain file reads, no other
+    program.  None when neither is visible."""
+    import torch
+
+    try:
+        dev = _device_sysfs()
+    except Exception:  # pragma: no cover - no device properties
+        dev = None
+    if dev is None:
+        return None
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-4)
+    for _ in range(int(seconds / one) + 1):
         step()
-        torch.cuda.synchronize()
-        one = max(time.perf_counter() - t0, 1e-4)
-        for _ in range(int(seconds / one) + 1):
-            step()
-        time.sleep(min(0.3, seconds / 3))
-        out = subprocess.run(["rocm-smi", "--showmetrics"], capture_output=True, text=True,
-                             timeout=20).stdout
-        torch.cuda.synchronize()
-    except (OSError, subprocess.SubprocessError):
+    mhz, watts = [], []
+    time.sleep(0.2 * seconds)
+    for _ in range(samples):
+        f, p = _sclk_mhz(dev), _power_w(dev)
+        if f:
+            mhz.append(f)
+        if p:
+            watts.append(p)
+        time.sleep(0.5 * seconds / samples)
+    torch.cuda.synchronize()
+    if not mhz and not watts:
         return None
-    power = re.search(r"current_socket_power \(W\): (\d+)", out)
-    clks = re.search(r"current_gfxclks \(MHz\): \[([0-9, ]+)\]", out)
-    if not clks:
-        return None
-    mhz = [int(x) for x in clks.group(1).split(",")]
-    return {"gfxclk_mhz": round(sum(mhz) / len(mhz)), "gfxclk_mhz_per_xcd": mhz,
-            "socket_power_w": int(power.group(1)) if power else None,
-            "source": "rocm-smi --showmetrics while the same launches run (outside the timed region)"}
+    mhz.sort()
+    watts.sort()
+    return {"gfxclk_mhz": mhz[len(mhz) // 2] if mhz else None,
+            "socket_power_w": round(watts[len(watts) // 2]) if watts else None,
+            "power_samples_w": [round(x) for x in watts],
+            "source": f"{dev}: pp_dpm_sclk, hwmon power1_*, read while the same launches "
+                      "run, outside the timed region; median of the samples"}
 
 
 def cpu_threads() -> int:
@@ -171,8 +241,20 @@ def main() -> int:
     lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, past_len=w.past_len)
+    if w.path == "splitkv":
+        n_splits = fa.fa_splitkv_splits(w.B, w.L, w.keys, w.H, w.Hkv, w.D, w.causal, w.past_len)
+        ws = torch.empty(fa.fa_splitkv_workspace_bytes(w.B, w.L, w.H, w.D, n_splits),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.forward_splitkv(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                               past_len=w.past_len, n_splits=n_splits, workspace=ws)
+    else:
+        n_splits = None
+
+        def step():
+            fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                       past_len=w.past_len)
 
     for _ in range(args.warmup):
         step()
@@ -198,8 +280,18 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
 
     value = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
     traffic = measured_traffic(name)
+    if w.path == "splitkv":
+        # decoding reads each K/V byte once and does ~1 flop per byte: HBM-bound
+        achieved = w.algorithmic_bytes / (kernel_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes": w.algorithmic_bytes}
+    else:
+        achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                    "traffic": traffic}
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -215,11 +307,11 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "L": w.L, "D": w.D,
                    "causal": w.causal, "layout": "BSHD", "seed": args.seed,
-                   **({"Lk": w.keys, "past_len": w.past_len} if w.keys != w.L else {})},
+                   **({"Lk": w.keys, "past_len": w.past_len} if w.keys != w.L else {}),
+                   **({"entry_point": "fa_fwd_splitkv", "n_splits": n_splits}
+                      if n_splits is not None else {})},
         "pct_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                     "traffic": traffic},
+        "roofline": roofline,
         "kernel_ms_mean": round(kernel_ms, 5),
         "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
         "kernel_sha": kernel_sha(),
@@ -228,7 +320,7 @@ def main() -> int:
           f"{value:.1f} TFLOP/s ({result['pct_peak']}% of {PEAK_FP16_TFLOPS})",
           file=sys.stderr, flush=True)
     clock = sample_clock_power(step)
-    if clock:
+    if clock and (clock["gfxclk_mhz"] or 0) >= 500 and w.path != "splitkv":
         # the published peak assumes 2.4 GHz; the same peak at the clock the part ran
         peak_at_clock = PEAK_FP16_TFLOPS * clock["gfxclk_mhz"] / 2400.0
         clock["peak_at_clock_tflops"] = round(peak_at_clock, 1)

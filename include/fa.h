@@ -47,7 +47,9 @@ enum fa_status {
     FA_ERR_ALIGN = 6,    /* a tensor pointer is not 16-byte aligned (lse: 4-byte)  */
     FA_ERR_ALIAS = 7,    /* the byte range of o or lse overlaps q, k, v or each other */
     FA_ERR_LAUNCH = 8,   /* the HIP runtime rejected the launch                    */
-    FA_ERR_DEVICE = 9    /* the current device could not be queried                */
+    FA_ERR_DEVICE = 9,   /* the current device could not be queried                */
+    FA_ERR_WORKSPACE = 10 /* fa_fwd_splitkv: workspace NULL, too small or not
+                             16-byte aligned                                       */
 };
 
 /*
@@ -112,11 +114,64 @@ FA_API int fa_fwd_kv(const void *q, const void *k, const void *v, void *o, float
               int B, int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len,
               float scale, hipStream_t stream);
 
+/*
+ * fa_fwd_splitkv -- the same operation as fa_fwd_kv, computed by splitting
+ * the key sequence (flash decoding; page "TileLang性能分析报告：H100上
+ * FlashAttention吞吐量达1.2PFlops", section "生产环境部署建议", which names it
+ * for inference).  Meant for few query rows against many keys (decoding one
+ * or a few tokens after a long cache), where the forward kernel's work items
+ * -- one per block of query rows -- are too few to fill the GPU.
+ *
+ * Each of n_splits contiguous ranges of the visible keys is processed by
+ * separate wavefronts, which write a partial result per query row and split
+ * p: LSE_p = ln sum_{j in p} exp(s_j) and O_p = sum_{j in p} exp(s_j - LSE_p)
+ * V_j (fp32).  A second kernel merges them exactly:
+ *   LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p,
+ * taking the largest LSE_p out first.  The per-split arithmetic (fp16
+ * products with fp32 accumulation, fp32 online softmax, fp16 probabilities
+ * into the second product) is that of fa_fwd; only the summation order over
+ * keys differs.  Mask, past_len, empty rows (O = 0, LSE = -inf) and the
+ * output rounding are as for fa_fwd_kv.
+ *
+ * Arguments q .. stream as for fa_fwd_kv, plus:
+ * n_splits   number of key splits, 1..4096; 0 = the library's choice,
+ *            fa_splitkv_splits(...).  Splits left empty by the mask or by
+ *            rounding contribute nothing.
+ * workspace  device pointer, 16-byte aligned, at least
+ *            fa_splitkv_workspace_bytes(B, Lq, H, D, n_splits) bytes (with
+ *            n_splits after the substitution of 0), owned by the caller,
+ *            overwritten by the call; it must not overlap any other buffer.
+ *            Calls that share a workspace must be ordered on one stream.
+ * workspace_bytes  its size.
+ *
+ * Errors: those of fa_fwd_kv; FA_ERR_SHAPE for n_splits outside 0..4096;
+ * FA_ERR_WORKSPACE for a NULL, short or misaligned workspace; FA_ERR_ALIAS
+ * when it overlaps another buffer.  B == 0 or Lq == 0 returns FA_OK and
+ * launches nothing (the workspace may then be NULL).
+ */
+FA_API int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int B, int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len,
+                          float scale, int n_splits, void *workspace, long long workspace_bytes,
+                          hipStream_t stream);
+
+/* The number of key splits fa_fwd_splitkv uses when passed n_splits = 0:
+ * about 1024 work items over the GPU, no split shorter than 128 keys, at
+ * least 1.  Pure host arithmetic; never fails. */
+FA_API int fa_splitkv_splits(int B, int Lq, int Lk, int H, int Hkv, int D, int causal,
+                             int past_len);
+
+/* Workspace bytes fa_fwd_splitkv needs: B*H*Lq*n_splits*(D + 1)*4 (fp32
+ * partial outputs [B][H][Lq][n_splits][D], then partial LSEs
+ * [B][H][Lq][n_splits]).  -1 for invalid arguments (a negative size, D not
+ * 64 or 128, n_splits outside 1..4096) or int64 overflow. */
+FA_API long long fa_splitkv_workspace_bytes(int B, int Lq, int H, int D, int n_splits);
+
 /* Human-readable name of an fa_status value (static storage, never NULL). */
 FA_API const char *fa_status_string(int status);
 
 /* Version of this ABI (bumped when an entry point is added or a signature or
- * a layout changes): 2 = fa_fwd, fa_fwd_kv. */
+ * a layout changes): 2 = fa_fwd, fa_fwd_kv; 3 adds fa_fwd_splitkv,
+ * fa_splitkv_splits and fa_splitkv_workspace_bytes. */
 FA_API int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,7 +35,8 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = fa.library()
     names = declared_symbols()
-    assert set(names) == {"fa_fwd", "fa_fwd_kv", "fa_status_string", "fa_abi_version"}
+    assert set(names) == {"fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv", "fa_splitkv_splits",
+                          "fa_splitkv_workspace_bytes", "fa_status_string", "fa_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], check=True,
                          stdout=subprocess.PIPE, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -44,7 +45,7 @@ def test_library_loads_and_exports_header_symbols():
         assert hasattr(lib, n)
     # nothing beyond the declared C ABI leaks out of the library
     assert exported == set(names)
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == 3
 
 
 def test_status_strings():
@@ -176,3 +177,69 @@ def test_binding_routes_unequal_lengths_to_the_kv_entry_point(monkeypatch):
     seen.clear()
     fa.forward(q, q, q, causal=True, out=o, with_lse=False)
     assert "fwd" in seen and "kv" not in seen
+
+
+# ------------------------------------------------------------ split-KV ABI
+
+WS = 0x60000000
+SPLIT_ARGS = dict(KV_ARGS, Lq=4, Lk=4096, past_len=4092, n_splits=8, workspace=WS,
+                  workspace_bytes=1 << 20)
+
+
+def call_split(**kw):
+    a = dict(SPLIT_ARGS)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                             a["H"], a["Hkv"], a["D"], a["causal"], a["past_len"], a["scale"],
+                             a["n_splits"], a["workspace"], a["workspace_bytes"], a["stream"])
+
+
+def test_splitkv_workspace_bytes():
+    # fp32 partial outputs [B][H][Lq][n][D] then partial LSEs [B][H][Lq][n]
+    assert fa.fa_splitkv_workspace_bytes(2, 3, 4, 128, 5) == 2 * 3 * 4 * 5 * (128 + 1) * 4
+    assert fa.fa_splitkv_workspace_bytes(1, 1, 1, 64, 1) == 65 * 4
+    assert fa.fa_splitkv_workspace_bytes(0, 1, 1, 64, 1) == 0
+    for bad in [dict(D=96), dict(n=0), dict(n=4097), dict(B=-1)]:
+        a = dict(B=1, Lq=1, H=1, D=64, n=1)
+        a.update(bad)
+        assert fa.fa_splitkv_workspace_bytes(a["B"], a["Lq"], a["H"], a["D"], a["n"]) == -1
+    big = 1 << 30
+    assert fa.fa_splitkv_workspace_bytes(big, big, big, 128, 4096) == -1  # int64 overflow
+
+
+def test_splitkv_default_splits():
+    # about 1024 work items, no split shorter than four 32-key blocks
+    assert fa.fa_splitkv_splits(8, 1, 8192, 32, 8, 128, 0, 0) == 16   # 64 items per split
+    assert fa.fa_splitkv_splits(1, 1, 256, 8, 8, 128, 0, 0) == 2      # capped by 8 blocks / 4
+    assert fa.fa_splitkv_splits(1, 1, 64, 8, 8, 128, 0, 0) == 1       # never below 1
+    assert fa.fa_splitkv_splits(64, 64, 4096, 32, 32, 128, 0, 0) == 1  # enough items already
+    # causal: only keys up to the last query's position count
+    assert fa.fa_splitkv_splits(1, 1, 1 << 20, 1, 1, 64, 1, 4095) == 32
+    assert fa.fa_splitkv_splits(1, 1, 1 << 20, 1, 1, 64, 0, 4095) == 1024
+    assert fa.fa_splitkv_splits(1, 1, 1 << 22, 1, 1, 64, 0, 0) == 1024
+    assert fa.fa_splitkv_splits(0, 1, 100, 1, 1, 64, 0, 0) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(Lk=-1), 2), (dict(H=3, Hkv=2), 3),
+    (dict(D=96), 4), (dict(scale=math.nan), 5), (dict(v=V + 2), 6),
+    (dict(n_splits=-1), 2), (dict(n_splits=4097), 2),
+    (dict(workspace=None), 10), (dict(workspace=WS + 8), 10),
+    (dict(workspace_bytes=4 * 2 * 8 * 65 * 4 - 1), 10),
+    (dict(workspace=Q), 7), (dict(workspace=O - 1024), 7), (dict(workspace=LSE + 16), 7),
+    (dict(workspace=K + 4096 * 2 * 64 * 2 - 16), 7),
+])
+def test_splitkv_invalid_arguments_rejected_without_launch(kw, status):
+    assert call_split(**kw) == status
+
+
+def test_splitkv_exact_workspace_size_accepted_by_validation():
+    """The documented size is enough: validation passes it (a NULL stream and
+    fake pointers would then reach the launch, so only the checks before it
+    are exercised, via a size one byte short being rejected above and the
+    empty problem here)."""
+    need = fa.fa_splitkv_workspace_bytes(1, 4, 2, 64, 8)
+    assert need == 4 * 2 * 8 * 65 * 4
+    assert call_split(Lq=0, workspace=None, workspace_bytes=0) == 0
+    assert call_split(B=0, workspace=None, workspace_bytes=0) == 0
+    assert call_split(B=0, n_splits=5000) == 2  # still validated

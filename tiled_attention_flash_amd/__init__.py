@@ -12,6 +12,12 @@ Returns o ``[B, Lq, H, D]`` fp16 and lse ``[B, H, Lq]`` fp32 (natural-log
 log-sum-exp of each row's scaled scores).  With Lq != Lk (or an explicit
 ``past_len``) query row i sits at key position i + past_len, default
 Lk - Lq, which the causal mask uses.
+
+    o, lse = tiled_attention_flash_amd.forward_splitkv(q, k, v, causal=False, scale=None)
+
+computes the same result by splitting the keys over separate wavefronts and
+merging the partial results (for few query rows against many keys); its fp32
+workspace is allocated with torch unless one is passed.
 """
 from __future__ import annotations
 
@@ -19,8 +25,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "fa_fwd", "fa_fwd_kv", "fa_status_string", "library", "library_path",
-           "FaError", "STATUS"]
+__all__ = ["forward", "forward_splitkv", "fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv",
+           "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_status_string", "library",
+           "library_path", "FaError", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa.so")
@@ -29,7 +36,7 @@ _lib = None
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_SHAPE", 3: "FA_ERR_GQA", 4: "FA_ERR_HEADDIM",
     5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_LAUNCH",
-    9: "FA_ERR_DEVICE",
+    9: "FA_ERR_DEVICE", 10: "FA_ERR_WORKSPACE",
 }
 
 
@@ -57,6 +64,13 @@ def library():
     lib.fa_fwd.restype = c_int
     lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 8 + [ctypes.c_float, vp]
     lib.fa_fwd_kv.restype = c_int
+    lib.fa_fwd_splitkv.argtypes = ([vp, vp, vp, vp, vp] + [c_int] * 8 + [ctypes.c_float, c_int, vp,
+                                                                          ctypes.c_longlong, vp])
+    lib.fa_fwd_splitkv.restype = c_int
+    lib.fa_splitkv_splits.argtypes = [c_int] * 8
+    lib.fa_splitkv_splits.restype = c_int
+    lib.fa_splitkv_workspace_bytes.argtypes = [c_int] * 5
+    lib.fa_splitkv_workspace_bytes.restype = ctypes.c_longlong
     lib.fa_status_string.argtypes = [c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -82,10 +96,26 @@ def fa_fwd_kv(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, st
                                    int(D), int(bool(causal)), int(past_len), float(scale), stream))
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
-            with_lse: bool = True, past_len: int | None = None):
-    """Attention forward on the current stream.  Returns (o, lse); lse is None
-    when ``with_lse`` is False and no ``lse`` buffer is given."""
+def fa_fwd_splitkv(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, n_splits,
+                   workspace, workspace_bytes, stream) -> int:
+    """Direct call of the split-KV entry point; status returned unchanged."""
+    return int(library().fa_fwd_splitkv(q, k, v, o, lse, int(B), int(Lq), int(Lk), int(H),
+                                        int(Hkv), int(D), int(bool(causal)), int(past_len),
+                                        float(scale), int(n_splits), workspace,
+                                        int(workspace_bytes), stream))
+
+
+def fa_splitkv_splits(B, Lq, Lk, H, Hkv, D, causal, past_len) -> int:
+    return int(library().fa_splitkv_splits(int(B), int(Lq), int(Lk), int(H), int(Hkv), int(D),
+                                           int(bool(causal)), int(past_len)))
+
+
+def fa_splitkv_workspace_bytes(B, Lq, H, D, n_splits) -> int:
+    return int(library().fa_splitkv_workspace_bytes(int(B), int(Lq), int(H), int(D),
+                                                    int(n_splits)))
+
+
+def _check_qkv(q, k, v):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -94,14 +124,16 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         if t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous 4-D [B, L, heads, D] tensor")
     B, L, H, D = q.shape
-    Lk = k.shape[1]
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
-    Hkv = k.shape[2]
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
+
+
+def _outputs(q, out, lse, with_lse):
+    import torch
+
+    B, L, H, _ = q.shape
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous() or out.device != q.device:
@@ -111,6 +143,55 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     elif lse is not None and (lse.shape != (B, H, L) or lse.dtype != torch.float32 or
                               not lse.is_contiguous() or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 [B, H, L] tensor on q's device")
+    return out, lse
+
+
+def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                    with_lse: bool = True, past_len: int | None = None,
+                    n_splits: int | None = None, workspace=None):
+    """The forward pass by key splits plus a merge (fa_fwd_splitkv), on the
+    current stream.  ``n_splits`` None lets the library choose; ``workspace``
+    (a CUDA tensor of at least ``fa_splitkv_workspace_bytes`` bytes) is
+    allocated here when not given.  Returns (o, lse) as ``forward`` does."""
+    import torch
+
+    _check_qkv(q, k, v)
+    B, L, H, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out, lse = _outputs(q, out, lse, with_lse)
+    past = Lk - L if past_len is None else int(past_len)
+    splits = fa_splitkv_splits(B, L, Lk, H, Hkv, D, causal, past) if n_splits is None else int(n_splits)
+    need = fa_splitkv_workspace_bytes(B, L, H, D, max(splits, 1))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    ptrs = (q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
+            out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd_splitkv(*ptrs, B, L, Lk, H, Hkv, D, causal, past, scale, splits,
+                            workspace.data_ptr() or None, ws_bytes, stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out, lse
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            with_lse: bool = True, past_len: int | None = None):
+    """Attention forward on the current stream.  Returns (o, lse); lse is None
+    when ``with_lse`` is False and no ``lse`` buffer is given."""
+    import torch
+
+    _check_qkv(q, k, v)
+    B, L, H, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out, lse = _outputs(q, out, lse, with_lse)
     past = Lk - L if past_len is None else int(past_len)
     ptrs = (q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
             out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None)

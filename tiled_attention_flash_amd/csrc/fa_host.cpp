@@ -28,10 +28,13 @@ bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
 
 bool misaligned(const void *p, uintptr_t to) { return ((uintptr_t)p & (to - 1)) != 0; }
 
-// Shared validation and dispatch of both entry points.
-int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Lq, int Lk,
-            int H, int Hkv, int D, int causal, int past_len, float scale, hipStream_t stream)
+// Shared argument validation of every entry point.  Returns FA_OK with *p
+// filled in, FA_OK with *empty set when there is nothing to compute, or an
+// error status.
+int validate(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Lq, int Lk,
+             int H, int Hkv, int D, int causal, int past_len, float scale, fa::Problem *p, bool *empty)
 {
+    *empty = false;
     if (B < 0 || Lq < 0 || Lk < 0 || H < 0 || Hkv < 0 || D < 0) return FA_ERR_SHAPE;
     if (H <= 0 || Hkv <= 0 || H % Hkv != 0) return FA_ERR_GQA;
     if (D != 64 && D != 128) return FA_ERR_HEADDIM;
@@ -46,7 +49,10 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
     if (q_elems < 0 || kv_elems < 0 || lse_elems < 0 || q_elems > INT64_MAX / 4 ||
         kv_elems > INT64_MAX / 4)
         return FA_ERR_SHAPE;
-    if (B == 0 || Lq == 0) return FA_OK;  // nothing to compute; pointers may be null
+    if (B == 0 || Lq == 0) {  // nothing to compute; pointers may be null
+        *empty = true;
+        return FA_OK;
+    }
 
     if (!q || !o || (Lk > 0 && (!k || !v))) return FA_ERR_NULLPTR;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
@@ -60,8 +66,45 @@ int forward(const void *q, const void *k, const void *v, void *o, float *lse, in
         overlaps(lse, lse_bytes, v, kv_bytes))
         return FA_ERR_ALIAS;
 
-    fa::Problem p{q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal != 0, causal ? past_len : 0, scale};
+    *p = fa::Problem{q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal != 0, causal ? past_len : 0, scale};
+    return FA_OK;
+}
+
+int forward(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Lq, int Lk,
+            int H, int Hkv, int D, int causal, int past_len, float scale, hipStream_t stream)
+{
+    fa::Problem p;
+    bool empty;
+    const int st = validate(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, &p, &empty);
+    if (st != FA_OK || empty) return st;
     return fa::launch_forward(p, stream);
+}
+
+// Keys that some query row can see: all Lk, or (causal) up to the last
+// query's position Lq - 1 + past_len.
+int64_t visible_keys(int Lq, int Lk, int causal, int past_len)
+{
+    if (!causal) return Lk;
+    const int64_t last = (int64_t)Lq + past_len;  // one past the last visible key
+    return last < 0 ? 0 : (last < Lk ? last : Lk);
+}
+
+constexpr int kMaxSplits = 4096;
+
+// The library's choice of key splits: enough (b, kv head, row block, split)
+// work items to give each of the 256 compute units about four, but no split
+// shorter than four 32-key blocks.
+int default_splits(int B, int Lq, int Lk, int H, int Hkv, int causal, int past_len)
+{
+    if (B <= 0 || Lq <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0) return 1;
+    const int64_t rows = (int64_t)Lq * (H / Hkv);
+    const int64_t base = (int64_t)B * Hkv * ((rows + 31) / 32);
+    const int64_t blocks = (visible_keys(Lq, Lk, causal, past_len) + 31) / 32;
+    int64_t n = (1024 + base - 1) / base;
+    const int64_t cap = blocks / 4;
+    if (n > cap) n = cap;
+    if (n < 1) n = 1;
+    return (int)(n > kMaxSplits ? kMaxSplits : n);
 }
 
 }  // namespace
@@ -79,6 +122,46 @@ extern "C" int fa_fwd_kv(const void *q, const void *k, const void *v, void *o, f
     return forward(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, stream);
 }
 
+extern "C" int fa_splitkv_splits(int B, int Lq, int Lk, int H, int Hkv, int D, int causal,
+                                 int past_len)
+{
+    (void)D;
+    return default_splits(B, Lq, Lk, H, Hkv, causal, past_len);
+}
+
+extern "C" long long fa_splitkv_workspace_bytes(int B, int Lq, int H, int D, int n_splits)
+{
+    if (B < 0 || Lq < 0 || H < 0 || (D != 64 && D != 128) || n_splits < 1 || n_splits > kMaxSplits)
+        return -1;
+    const int64_t rows = elems4(B, H, Lq, 1);
+    if (rows < 0) return -1;
+    return (long long)fa::splitkv_workspace_bytes(rows, n_splits, D);
+}
+
+extern "C" int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int B, int Lq, int Lk, int H, int Hkv, int D, int causal,
+                              int past_len, float scale, int n_splits, void *workspace,
+                              long long workspace_bytes, hipStream_t stream)
+{
+    fa::Problem p;
+    bool empty;
+    const int st = validate(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, &p, &empty);
+    if (st != FA_OK) return st;
+    if (n_splits < 0 || n_splits > kMaxSplits) return FA_ERR_SHAPE;
+    if (empty) return FA_OK;
+    if (n_splits == 0) n_splits = default_splits(B, Lq, Lk, H, Hkv, causal, past_len);
+    const int64_t need = fa::splitkv_workspace_bytes(elems4(B, H, Lq, 1), n_splits, D);
+    if (need < 0) return FA_ERR_SHAPE;
+    if (!workspace || workspace_bytes < need || misaligned(workspace, 16)) return FA_ERR_WORKSPACE;
+    const int64_t q_bytes = elems4(B, Lq, H, D) * 2, kv_bytes = elems4(B, Lk, Hkv, D) * 2;
+    const int64_t lse_bytes = elems4(B, H, Lq, 1) * 4;
+    if (overlaps(workspace, need, q, q_bytes) || overlaps(workspace, need, k, kv_bytes) ||
+        overlaps(workspace, need, v, kv_bytes) || overlaps(workspace, need, o, q_bytes) ||
+        overlaps(workspace, need, lse, lse_bytes))
+        return FA_ERR_ALIAS;
+    return fa::launch_splitkv(p, n_splits, workspace, stream);
+}
+
 extern "C" const char *fa_status_string(int status)
 {
     switch (status) {
@@ -92,8 +175,11 @@ extern "C" const char *fa_status_string(int status)
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: o or lse overlaps another tensor";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
     case FA_ERR_DEVICE: return "FA_ERR_DEVICE: could not query the current device";
+    case FA_ERR_WORKSPACE:
+        return "FA_ERR_WORKSPACE: workspace is NULL, smaller than fa_splitkv_workspace_bytes, "
+               "or not 16-byte aligned";
     default: return "FA_ERR_UNKNOWN";
     }
 }
 
-extern "C" int fa_abi_version(void) { return 2; }
+extern "C" int fa_abi_version(void) { return 3; }

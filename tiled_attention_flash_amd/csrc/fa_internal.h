@@ -24,4 +24,11 @@ struct Problem {
 // Enqueues the forward kernels on `stream`.  Returns FA_OK or FA_ERR_LAUNCH.
 int launch_forward(const Problem &p, hipStream_t stream);
 
+// Split-KV forward: bytes of fp32 workspace for rows_total = B*H*Lq output
+// rows and n_splits key splits (-1 on overflow), and the launcher of the
+// split kernel plus the merge kernel.  Returns FA_OK, FA_ERR_SHAPE or
+// FA_ERR_LAUNCH.
+int64_t splitkv_workspace_bytes(int64_t rows_total, int64_t n_splits, int D);
+int launch_splitkv(const Problem &p, int n_splits, void *workspace, hipStream_t stream);
+
 }  // namespace fa

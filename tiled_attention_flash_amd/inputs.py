@@ -32,6 +32,7 @@ class Workload:
     causal: bool
     qk_mult: float = 1.0  # Q and K are multiplied by this before the fp16 cast
     Lk: int | None = None  # key rows; None = L (queries and keys equally long)
+    path: str = "forward"  # entry point that computes it: "forward" or "splitkv"
 
     @property
     def Lq(self) -> int:
@@ -82,6 +83,11 @@ WORKLOADS = {
     # 1024 new queries after 3072 cached positions (a prefill continuing a prefix)
     "prefill-b8-h32-q1024-kv4096-d128-causal": Workload(
         "prefill-b8-h32-q1024-kv4096-d128-causal", 8, 32, 32, 1024, 128, True, 1.0, 4096),
+    # one new query per sequence after a long cache (decoding), by key splits
+    "decode-b8-h32-kv8-q1-k32768-d128-causal": Workload(
+        "decode-b8-h32-kv8-q1-k32768-d128-causal", 8, 32, 8, 1, 128, True, 1.0, 32768, "splitkv"),
+    "decode-b8-h32-q1-k4096-d128-causal": Workload(
+        "decode-b8-h32-q1-k4096-d128-causal", 8, 32, 32, 1, 128, True, 1.0, 4096, "splitkv"),
 }
 
 HEADLINE = "mha-b8-h32-L4096-d128"
