@@ -36,6 +36,11 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kSB = 32;               // keys per score block (one 32x32 accumulator)
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
+// A lane's sum of the fp16 probabilities of one score block at or above which
+// the block is recomputed against its own maximum.  Every kept probability
+// is then below 2^15, far from fp16's largest finite value (65504), and a
+// probability that overflowed to inf always fails the test.
+constexpr float kSumLimit = 32768.0f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -259,6 +264,21 @@ struct WaveMath {
             st.m = m_new;
             st.mc = m_new == -__builtin_huge_valf() ? 0.0f : m_new * c;
         }
+    }
+
+    // Raise the reference maximum to at least mx (per lane) and rescale O
+    // and l to it; a lane whose maximum does not change keeps factor 1.
+    __device__ __forceinline__ static void raise_to(State &st, float mx, float c)
+    {
+        const float m_new = fmaxf(st.m, mx);
+        const float sf = st.m == m_new ? 1.0f : exp2_fast((st.m - m_new) * c);
+        st.l *= sf;
+#pragma unroll
+        for (int i = 0; i < kDBlocks; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[i][r] *= sf;
+        st.m = m_new;
+        st.mc = m_new == -__builtin_huge_valf() ? 0.0f : m_new * c;
     }
 
     // P = exp2(S*c - m*c) for score pair p (registers 2p, 2p+1), rounded to

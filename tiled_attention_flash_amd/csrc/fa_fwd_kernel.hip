@@ -150,43 +150,57 @@ template <int D, bool CAUSAL, int W>
 struct Kernel : WaveMath<D, CAUSAL> {
     using M = WaveMath<D, CAUSAL>;
     using typename M::State;
-    using typename M::MaxTree;
     using M::kSteps;
     using M::kDBlocks;
     using M::kCS;
     using M::kPairs;
     using M::kfrag;
     using M::vfrag;
-    using M::needs_mask;
     using M::mask;
     using M::block_max;
     using M::s_product;
     using M::rescale;
+    using M::raise_to;
     using M::exp_pair;
     using G = Geo<D, W>;
     static constexpr int kThreads = 64 * W;
     static constexpr int kBM = 32 * W;  // query rows per work item
-    static constexpr int kPairsA = 6;   // pairs exponentiated beside the S product
 
-    // One pipelined step for score block u (scores sc, reference maximum
-    // already taken): the S product of block u+1 (into sn, when NEXT) runs
-    // interleaved with the exponentials of block u, then the P.V product of
-    // block u runs beside the last exponentials, and the row maximum of
-    // block u+1 (masked first when mask_next) is returned in mx_next.  The
-    // matrix unit always has work that does not wait on the vector ALU and
-    // vice versa.  kl: first K row of block u+1, vl: first V row of block u.
-    template <bool NEXT>
-    __device__ __forceinline__ static void body(State &st, const floatx16 &sc, floatx16 &sn,
-                                                const _Float16 *kl, const _Float16 *vl,
-                                                bool mask_next, int k0_next, int Lk, int qp, float c,
-                                                float &mx_next)
+    // The probabilities of a block overran the limit: raise the reference
+    // maximum to the block's own (rescaling O and l) and compute them again.
+    __device__ __forceinline__ static void fixup(State &st, const floatx16 &sc, half8 (&pf)[kCS],
+                                                           float (&rs)[2], float c)
     {
+        raise_to(st, block_max(sc), c);
+        rs[0] = 0.0f;
+        rs[1] = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) exp_pair(sc, pf, rs, p, st.mc, c);
+    }
+
+    // One pipelined step for score block u, whose scores sc are complete.
+    // MASK: mask sc first (the block holds keys past the end, or, causal,
+    // keys after some row's position).  NEXT: the S product of block u+1
+    // (into sn) is issued with the exponentials of block u between its
+    // MFMAs, so the matrix unit always has work that does not wait on the
+    // vector ALU.  The probabilities are taken against the current reference
+    // maximum with no row maximum of their own; one wavefront-wide test of
+    // the lanes' block sums sends the rare block that overruns the limit to
+    // `fixup` before any of it reaches O.  Then the P.V product of block u.
+    // kl: first K row of block u+1, vl: first V row of block u.
+    template <bool NEXT, bool MASK>
+    __device__ __forceinline__ static void step(State &st, floatx16 &sc, floatx16 &sn,
+                                                const _Float16 *kl, const _Float16 *vl, int k0,
+                                                int Lk, int qp, float c)
+    {
+        if constexpr (MASK) mask(sc, k0, Lk, qp);
         half8 pf[kCS];
         float rs[2] = {0.0f, 0.0f};
         const float mc = st.mc;
+        constexpr int kN = kDBlocks * kCS;
+        constexpr int kVAhead = 4;
+        half8 va[kN];
 
-        // S(u+1) = K(u+1) . Q^T beside pairs [0, kPairsA) of block u; K
-        // fragments are requested kAhead k-steps before their MFMAs
         if constexpr (NEXT) {
             constexpr int kAhead = kSteps < 4 ? kSteps : 4;
             half8 ka[kSteps];
@@ -198,69 +212,28 @@ struct Kernel : WaveMath<D, CAUSAL> {
                 if (s + kAhead < kSteps) ka[s + kAhead] = kfrag(st, kl, s + kAhead);
                 sn = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[s], st.qf[s], sn, 0, 0, 0);
 #pragma unroll
-                for (int p = kPairsA * s / kSteps; p < kPairsA * (s + 1) / kSteps; ++p)
+                for (int p = kPairs * s / kSteps; p < kPairs * (s + 1) / kSteps; ++p)
                     exp_pair(sc, pf, rs, p, mc, c);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
-            for (int p = 0; p < kPairsA; ++p) exp_pair(sc, pf, rs, p, mc, c);
+            for (int p = 0; p < kPairs; ++p) exp_pair(sc, pf, rs, p, mc, c);
         }
-
-        // O^T += V^T . P^T, k-step-major so that the operand holding the
-        // remaining pairs is needed last; V operands kVAhead MFMAs ahead.
-        // From MFMA 2 on (S(u+1) has completed by then) the row maximum of
-        // block u+1 is taken in stages beside the MFMAs.
-        constexpr int kN = kDBlocks * kCS;
-        constexpr int kVAhead = 4;
-        constexpr int kMaxFrom = 2;
-        half8 va[kN];
-        MaxTree mt;
+        // V operands of the first P.V MFMAs in flight during the test
 #pragma unroll
         for (int n = 0; n < kVAhead; ++n) va[n] = vfrag(st, vl, n % kDBlocks, n / kDBlocks);
+        if (__builtin_amdgcn_ballot_w64(rs[0] + rs[1] >= kSumLimit)) fixup(st, sc, pf, rs, c);
+        st.l += rs[0] + rs[1];
+
+        // O^T += V^T . P^T, V operands kVAhead MFMAs ahead
 #pragma unroll
         for (int n = 0; n < kN; ++n) {
             if (n + kVAhead < kN) va[n + kVAhead] = vfrag(st, vl, (n + kVAhead) % kDBlocks, (n + kVAhead) / kDBlocks);
-            if (kPairsA + n < kPairs) exp_pair(sc, pf, rs, kPairsA + n, mc, c);
-            if constexpr (NEXT) {
-                if (n == kMaxFrom && mask_next) mask(sn, k0_next, Lk, qp);
-                if (n >= kMaxFrom) {
-                    constexpr int kSlots = kN - kMaxFrom;
-#pragma unroll
-                    for (int g = MaxTree::kStages * (n - kMaxFrom) / kSlots;
-                         g < MaxTree::kStages * (n - kMaxFrom + 1) / kSlots; ++g)
-                        mt.stage(g, sn);
-                }
-            }
             st.oacc[n % kDBlocks] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pf[n / kDBlocks],
                                                                             st.oacc[n % kDBlocks], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        st.l += rs[0] + rs[1];
-        if constexpr (NEXT) mx_next = mt.mx;
-    }
-
-    // Score block u (keys 32u..32u+31) followed by block u+1.  Under the
-    // causal mask a block past a wavefront's diagonal is still computed, with
-    // every score masked to -inf: its weights are exactly 0 and the reference
-    // maximum is unchanged, so the result is the same as skipping it, and
-    // every wavefront of the workgroup runs the same straight-line code.
-    __device__ __forceinline__ static void block_next(State &st, const floatx16 &sc, floatx16 &sn,
-                                                      const _Float16 *kl, const _Float16 *vl, int u,
-                                                      int Lk, int wp0, int qp, float c)
-    {
-        const int k0n = kSB * (u + 1);
-        float mx;
-        body<true>(st, sc, sn, kl, vl, needs_mask(k0n, Lk, wp0), k0n, Lk, qp, c, mx);
-        rescale(st, mx, c);
-    }
-
-    // the last score block of the work item
-    __device__ __forceinline__ static void block_last(State &st, const floatx16 &sc, floatx16 &sn,
-                                                      const _Float16 *vl, int Lk, int qp, float c)
-    {
-        float mx;
-        body<false>(st, sc, sn, nullptr, vl, false, 0, Lk, qp, c, mx);
     }
 
     // LDS tile t (P = t % 2) covers score blocks u = 2t (scores in sa) and
@@ -284,37 +257,36 @@ struct Kernel : WaveMath<D, CAUSAL> {
         if (t + 1 < n_tiles) issue_loads<D, W, true>(lo, vbase, kv_row, kBN * (t + 1), Lk, vlds[P ^ 1]);
     }
 
-    // a tile whose two blocks both have a successor
-    template <int P>
+    // a tile whose two blocks both have a successor; MASK: mask both blocks
+    template <int P, bool MASK>
     __device__ __forceinline__ static void tile(State &st, floatx16 &sa, floatx16 &sb,
                                                 const LoadOffsets<D, W> &lo, const _Float16 *kbase,
                                                 const _Float16 *vbase, int64_t kv_row, int t,
-                                                int n_tiles, int n_blocks, int Lk, int wp0, int qp,
-                                                float c, _Float16 (*klds)[G::kTile],
-                                                _Float16 (*vlds)[G::kTile])
+                                                int n_tiles, int n_blocks, int Lk, int qp, float c,
+                                                _Float16 (*klds)[G::kTile], _Float16 (*vlds)[G::kTile])
     {
         tile_start<P>(lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, klds, vlds);
         const _Float16 *kl = klds[P ^ 1], *vl = vlds[P];
-        block_next(st, sa, sb, kl, vl, 2 * t, Lk, wp0, qp, c);
-        block_next(st, sb, sa, kl + kSB * D, vl + kSB * D, 2 * t + 1, Lk, wp0, qp, c);
+        step<true, MASK>(st, sa, sb, kl, vl, kBN * t, Lk, qp, c);
+        step<true, MASK>(st, sb, sa, kl + kSB * D, vl + kSB * D, kBN * t + kSB, Lk, qp, c);
     }
 
     // the final tile: block 2t+1, if it exists, is the last one
-    template <int P>
+    template <int P, bool MASK>
     __device__ __forceinline__ static void tile_final(State &st, floatx16 &sa, floatx16 &sb,
                                                       const LoadOffsets<D, W> &lo, const _Float16 *kbase,
                                                       const _Float16 *vbase, int64_t kv_row, int t,
-                                                      int n_tiles, int n_blocks, int Lk, int wp0, int qp,
-                                                      float c, _Float16 (*klds)[G::kTile],
+                                                      int n_tiles, int n_blocks, int Lk, int qp, float c,
+                                                      _Float16 (*klds)[G::kTile],
                                                       _Float16 (*vlds)[G::kTile])
     {
         tile_start<P>(lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, klds, vlds);
         const _Float16 *kl = klds[P ^ 1], *vl = vlds[P];
         if (2 * t + 1 < n_blocks) {
-            block_next(st, sa, sb, kl, vl, 2 * t, Lk, wp0, qp, c);
-            block_last(st, sb, sa, vl + kSB * D, Lk, qp, c);
+            step<true, MASK>(st, sa, sb, kl, vl, kBN * t, Lk, qp, c);
+            step<false, MASK>(st, sb, sa, nullptr, vl + kSB * D, kBN * t + kSB, Lk, qp, c);
         } else {
-            block_last(st, sa, sb, vl, Lk, qp, c);
+            step<false, MASK>(st, sa, sb, nullptr, vl, kBN * t, Lk, qp, c);
         }
     }
 
@@ -359,9 +331,8 @@ struct Kernel : WaveMath<D, CAUSAL> {
         State st;
         const int wq0 = q0 + 32 * wave;
         const int qi = wq0 + col;
-        // key positions of the wavefront's first query and of this lane's
-        // query; rows past the end (never written) take the last row's
-        const int wp0 = (wq0 < Lq ? wq0 : Lq - 1) + a.past_len;
+        // key position of this lane's query; rows past the end (never
+        // written) take the last row's
         const int qp = (qi < Lq ? qi : Lq - 1) + a.past_len;
         M::init(st);
 
@@ -384,31 +355,61 @@ struct Kernel : WaveMath<D, CAUSAL> {
             M::init_lds_bases(st);
             const float c = a.scale_log2;
 
-            // prologue: scores and reference maximum of block 0; K tile 0 in flight
+            // prologue: scores and exact reference maximum of block 0; K tile 0 in flight
             floatx16 sa, sb;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (n_blocks > 1) issue_loads<D, W, false>(lo, kbase, kv_row, kSB, Lk, klds[1]);
             s_product(sa, st, klds[0] + kSB * D);
-            if (needs_mask(0, Lk, wp0)) mask(sa, 0, Lk, qp);
+            mask(sa, 0, Lk, qp);
             rescale(st, block_max(sa), c);
 
-            // tiles t < n_main = n_tiles - 1 have a successor for both blocks;
-            // tile n_tiles - 1 holds the last block
+            // Tiles t < n_main have a successor for both blocks; tile
+            // n_tiles - 1 holds the last block.  The first t_clean tiles need
+            // no mask on any wavefront: every key is < Lk and (causal) at or
+            // before the position of the work item's first query row.
             const int n_main = (n_blocks - 1) / 2;
-            int t = 0;
-            for (; t + 1 < n_main; t += 2) {
-                tile<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
-                tile<1>(st, sa, sb, lo, kbase, vbase, kv_row, t + 1, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
+            int n_clean = Lk / kSB;
+            if (CAUSAL) {
+                const int first = q0 + a.past_len;  // position of the first query row
+                const int nc = first < 0 ? 0 : (first + 1) / kSB;
+                n_clean = nc < n_clean ? nc : n_clean;
             }
-            if (t < n_main) {
-                tile<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
+            const int t_clean = n_clean / 2 < n_main ? n_clean / 2 : n_main;
+            int t = 0;
+            for (; t + 1 < t_clean; t += 2) {
+                tile<0, false>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+                tile<1, false>(st, sa, sb, lo, kbase, vbase, kv_row, t + 1, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+            }
+            if (t < t_clean) {
+                tile<0, false>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
                 ++t;
             }
-            if (t & 1)
-                tile_final<1>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
-            else
-                tile_final<0>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, wp0, qp, c, klds, vlds);
+            if ((t & 1) && t < n_main) {
+                tile<1, true>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+                ++t;
+            }
+            for (; t + 1 < n_main; t += 2) {
+                tile<0, true>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+                tile<1, true>(st, sa, sb, lo, kbase, vbase, kv_row, t + 1, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+            }
+            if (t < n_main) {
+                tile<0, true>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+                ++t;
+            }
+            // the last tile needs no mask when its blocks are all clean
+            const bool mask_last = n_blocks > n_clean;
+            if (t & 1) {
+                if (mask_last)
+                    tile_final<1, true>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+                else
+                    tile_final<1, false>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+            } else {
+                if (mask_last)
+                    tile_final<0, true>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+                else
+                    tile_final<0, false>(st, sa, sb, lo, kbase, vbase, kv_row, t, n_tiles, n_blocks, Lk, qp, c, klds, vlds);
+            }
         }
 
         // ---- finalise: O = acc / l (guarded as on the page), LSE = scale*m + ln l
