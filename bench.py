@@ -55,101 +55,70 @@ def measured_traffic(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def _device_sysfs(dev_index: int = 0):
-    """The sysfs directory (`/sys/class/drm/cardN/device`) of the HIP device,
-    found through its PCI address; None when it is not visible."""
-    import glob
-
-    import torch
-
-    props = torch.cuda.get_device_properties(dev_index)
-    try:
-        addr = "%04x:%02x:%02x" % (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
-    except AttributeError:
-        addr = None
-    cands = []
-    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
-        pci = os.path.basename(os.path.realpath(d))
-        cands.append((pci, d))
-    for pci, d in cands:
-        if addr and pci.startswith(addr):
-            return d
-    return cands[0][1] if len(cands) == 1 else None
-
-
-def _read(path):
-    try:
-        with open(path) as f:
-            return f.read()
-    except OSError:
-        return None
-
-
-def _power_w(dev):
+def _power_w():
+    """Board power from the GPU's hwmon (power1_average, else power1_input),
+    plain sysfs reads; None where not visible."""
     import glob
 
     for name in ("power1_average", "power1_input"):
-        for p in glob.glob(os.path.join(dev, "hwmon", "hwmon*", name)):
-            t = _read(p)
-            if t and t.strip().isdigit() and int(t) > 0:
-                return int(t) / 1e6
+        for p in sorted(glob.glob(f"/sys/class/drm/card*/device/hwmon/hwmon*/{name}")):
+            try:
+                with open(p) as f:
+                    v = int(f.read().strip())
+            except (OSError, ValueError):
+                continue
+            if v > 0:
+                return v / 1e6
     return None
 
 
-def _sclk_mhz(dev):
-    """Current engine clock: the starred level of pp_dpm_sclk ("1: 2100Mhz *")."""
-    import re
+def sample_clock_power(step, seconds: float = 1.5, samples: int = 5):
+    """Shader clock and board power while the same launches run, outside the
+    timed region.  About `seconds` of launches are queued; meanwhile the
+    clock probe of libfa_clock.so (one wavefront on a side stream counting
+    shader cycles over a 200 us window of the 100 MHz real-time counter)
+    runs `samples` times, and hwmon power is read beside it.  Medians are
+    reported; None when the probe library is missing."""
+    import ctypes
 
-    t = _read(os.path.join(dev, "pp_dpm_sclk"))
-    if not t:
-        return None
-    for line in t.splitlines():
-        if line.rstrip().endswith("*"):
-            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
-            if m:
-                return int(m.group(1))
-    return None
-
-
-def sample_clock_power(step, seconds: float = 1.5, samples: int = 8):
-    """Engine clock and board power while the same launches run, outside the
-    timed region: about `seconds` of launches are queued, then the device's
-    sysfs files (`pp_dpm_sclk`, hwmon `power1_average` or `power1_input`) are
-    read `samples` times while they drain -- plain file reads, no other
-    program.  None when neither is visible."""
     import torch
 
-    try:
-        dev = _device_sysfs()
-    except Exception:  # pragma: no cover - no device properties
-        dev = None
-    if dev is None:
+    path = os.path.join(ROOT, "tiled_attention_flash_amd", "libfa_clock.so")
+    if not os.path.exists(path):
         return None
+    lib = ctypes.CDLL(path)
+    lib.fa_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_void_p]
+    lib.fa_clock_probe.restype = ctypes.c_int
+    # the result buffers are zeroed before the launches are queued: a fill
+    # queued behind them would land after the probes have written
+    side = torch.cuda.Stream()
+    bufs = [torch.zeros(2, dtype=torch.int64, device="cuda") for _ in range(samples)]
     t0 = time.perf_counter()
     step()
     torch.cuda.synchronize()
     one = max(time.perf_counter() - t0, 1e-4)
     for _ in range(int(seconds / one) + 1):
         step()
-    mhz, watts = [], []
-    time.sleep(0.2 * seconds)
-    for _ in range(samples):
-        f, p = _sclk_mhz(dev), _power_w(dev)
-        if f:
-            mhz.append(f)
+    watts = []
+    time.sleep(0.15 * seconds)
+    for b in bufs:
+        with torch.cuda.stream(side):
+            if lib.fa_clock_probe(b.data_ptr(), 20000, side.cuda_stream) != 0:
+                return None
+        p = _power_w()
         if p:
             watts.append(p)
-        time.sleep(0.5 * seconds / samples)
+        time.sleep(0.6 * seconds / samples)
     torch.cuda.synchronize()
-    if not mhz and not watts:
-        return None
-    mhz.sort()
+    mhz = sorted(100.0 * c / r for c, r in (b.tolist() for b in bufs) if r > 0)
     watts.sort()
-    return {"gfxclk_mhz": mhz[len(mhz) // 2] if mhz else None,
-            "socket_power_w": round(watts[len(watts) // 2]) if watts else None,
-            "power_samples_w": [round(x) for x in watts],
-            "source": f"{dev}: pp_dpm_sclk, hwmon power1_*, read while the same launches "
-                      "run, outside the timed region; median of the samples"}
+    if not mhz:
+        return None
+    return {"gfxclk_mhz": round(mhz[len(mhz) // 2]), "gfxclk_mhz_samples": [round(x) for x in mhz],
+            "board_power_w": round(watts[len(watts) // 2]) if watts else None,
+            "source": "libfa_clock.so probe (s_memtime cycles over a 100 MHz s_memrealtime window, "
+                      "side stream) and hwmon power, while the same launches run, outside the "
+                      "timed region; medians"}
 
 
 def cpu_threads() -> int:

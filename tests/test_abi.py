@@ -207,17 +207,41 @@ def test_splitkv_workspace_bytes():
     assert fa.fa_splitkv_workspace_bytes(big, big, big, 128, 4096) == -1  # int64 overflow
 
 
+def _splits_model(B, Lq, Lk, H, Hkv, D, causal, past_len):
+    """The documented choice: minimise rounds * (blocks per split + 2) over
+    1..min(64, blocks // 4) splits, rounds of 256 * (160 KiB // (384 * D))
+    resident work items; ties to fewer splits."""
+    if B <= 0 or Lq <= 0 or H <= 0 or Hkv <= 0 or H % Hkv or D not in (64, 128):
+        return 1
+    rows = Lq * (H // Hkv)
+    base = B * Hkv * ((rows + 31) // 32)
+    vis = Lk if not causal else max(0, min(Lk, Lq + past_len))
+    blocks = (vis + 31) // 32
+    slots = 256 * ((160 * 1024) // (384 * D))
+    cap = max(1, min(64, blocks // 4))
+    costs = [((base * n + slots - 1) // slots) * (-(-blocks // n) + 2) for n in range(1, cap + 1)]
+    return 1 + costs.index(min(costs))
+
+
 def test_splitkv_default_splits():
-    # about 1024 work items, no split shorter than four 32-key blocks
-    assert fa.fa_splitkv_splits(8, 1, 8192, 32, 8, 128, 0, 0) == 16   # 64 items per split
-    assert fa.fa_splitkv_splits(1, 1, 256, 8, 8, 128, 0, 0) == 2      # capped by 8 blocks / 4
-    assert fa.fa_splitkv_splits(1, 1, 64, 8, 8, 128, 0, 0) == 1       # never below 1
-    assert fa.fa_splitkv_splits(64, 64, 4096, 32, 32, 128, 0, 0) == 1  # enough items already
+    # hand-checked: 768 resident items at D = 128; 64 items per split -> 12 splits, one round
+    assert fa.fa_splitkv_splits(8, 1, 32768, 32, 8, 128, 1, 32767) == 12
+    # one query row of one K/V head over 2^17 keys: capped at 64 splits
+    assert fa.fa_splitkv_splits(1, 1, 131072, 32, 8, 128, 1, 131071) == 64
+    # 8 blocks: at most 2 splits of >= 4 blocks; 2 blocks: 1
+    assert fa.fa_splitkv_splits(1, 1, 256, 8, 8, 128, 0, 0) == 2
+    assert fa.fa_splitkv_splits(1, 1, 64, 8, 8, 128, 0, 0) == 1
     # causal: only keys up to the last query's position count
     assert fa.fa_splitkv_splits(1, 1, 1 << 20, 1, 1, 64, 1, 4095) == 32
-    assert fa.fa_splitkv_splits(1, 1, 1 << 20, 1, 1, 64, 0, 4095) == 1024
-    assert fa.fa_splitkv_splits(1, 1, 1 << 22, 1, 1, 64, 0, 0) == 1024
     assert fa.fa_splitkv_splits(0, 1, 100, 1, 1, 64, 0, 0) == 1
+    for B in (1, 2, 8, 32):
+        for Lq in (1, 3, 16, 64):
+            for Lk in (100, 4096, 32768, 200000):
+                for H, Hkv in ((32, 8), (32, 32), (8, 1)):
+                    for D in (64, 128):
+                        for causal in (0, 1):
+                            args = (B, Lq, Lk, H, Hkv, D, causal, Lk - Lq)
+                            assert fa.fa_splitkv_splits(*args) == _splits_model(*args), args
 
 
 @pytest.mark.parametrize("kw,status", [

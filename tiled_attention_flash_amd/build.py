@@ -14,6 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
+CLOCK_LIB = os.path.join(PKG, "libfa_clock.so")  # benchmark helper: shader clock probe
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are switched off for every HIP translation unit.
@@ -50,6 +51,7 @@ def build_shared(sources, out, include_dirs=(), extra=()) -> str:
 
 
 def build() -> str:
+    build_shared([os.path.join(CSRC, "fa_clock_probe.hip")], CLOCK_LIB)
     return build_shared([os.path.join(CSRC, s) for s in SOURCES], LIB, include_dirs=[INCLUDE, CSRC])
 
 

@@ -91,20 +91,36 @@ int64_t visible_keys(int Lq, int Lk, int causal, int past_len)
 
 constexpr int kMaxSplits = 4096;
 
-// The library's choice of key splits: enough (b, kv head, row block, split)
-// work items to give each of the 256 compute units about four, but no split
-// shorter than four 32-key blocks.
-int default_splits(int B, int Lq, int Lk, int H, int Hkv, int causal, int past_len)
+// The library's choice of key splits.  Each (b, kv head, row block, split)
+// work item is one wavefront holding a 3-stage ring of 32-key K and V tiles
+// in LDS (384*D bytes), so 160 KiB of LDS keeps `slots` of them resident on
+// the 256 compute units.  Work items run in rounds of `slots`; a round costs
+// about the split's length in 32-key blocks plus two blocks of fixed work,
+// and a last round that is only partly full costs as much as a full one.
+// The choice minimises rounds * (blocks per split + 2) over 1..64 splits
+// (the merge reads every split's partial result), with no split shorter
+// than four blocks; ties go to fewer splits.
+int default_splits(int B, int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len)
 {
-    if (B <= 0 || Lq <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0) return 1;
+    if (B <= 0 || Lq <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || (D != 64 && D != 128)) return 1;
     const int64_t rows = (int64_t)Lq * (H / Hkv);
     const int64_t base = (int64_t)B * Hkv * ((rows + 31) / 32);
     const int64_t blocks = (visible_keys(Lq, Lk, causal, past_len) + 31) / 32;
-    int64_t n = (1024 + base - 1) / base;
-    const int64_t cap = blocks / 4;
-    if (n > cap) n = cap;
-    if (n < 1) n = 1;
-    return (int)(n > kMaxSplits ? kMaxSplits : n);
+    const int64_t slots = 256 * ((160 * 1024) / (384 * D));
+    int64_t cap = blocks / 4;
+    if (cap > 64) cap = 64;
+    if (cap < 1) cap = 1;
+    int best = 1;
+    int64_t best_cost = -1;
+    for (int64_t n = 1; n <= cap; ++n) {
+        const int64_t rounds = (base * n + slots - 1) / slots;
+        const int64_t cost = rounds * ((blocks + n - 1) / n + 2);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = (int)n;
+        }
+    }
+    return best;
 }
 
 }  // namespace
@@ -125,8 +141,7 @@ extern "C" int fa_fwd_kv(const void *q, const void *k, const void *v, void *o, f
 extern "C" int fa_splitkv_splits(int B, int Lq, int Lk, int H, int Hkv, int D, int causal,
                                  int past_len)
 {
-    (void)D;
-    return default_splits(B, Lq, Lk, H, Hkv, causal, past_len);
+    return default_splits(B, Lq, Lk, H, Hkv, D, causal, past_len);
 }
 
 extern "C" long long fa_splitkv_workspace_bytes(int B, int Lq, int H, int D, int n_splits)
@@ -149,7 +164,7 @@ extern "C" int fa_fwd_splitkv(const void *q, const void *k, const void *v, void 
     if (st != FA_OK) return st;
     if (n_splits < 0 || n_splits > kMaxSplits) return FA_ERR_SHAPE;
     if (empty) return FA_OK;
-    if (n_splits == 0) n_splits = default_splits(B, Lq, Lk, H, Hkv, causal, past_len);
+    if (n_splits == 0) n_splits = default_splits(B, Lq, Lk, H, Hkv, D, causal, past_len);
     const int64_t need = fa::splitkv_workspace_bytes(elems4(B, H, Lq, 1), n_splits, D);
     if (need < 0) return FA_ERR_SHAPE;
     if (!workspace || workspace_bytes < need || misaligned(workspace, 16)) return FA_ERR_WORKSPACE;

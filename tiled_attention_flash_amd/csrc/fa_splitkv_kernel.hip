@@ -281,41 +281,73 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void fa_splitkv_
     SplitKernel<D, CAUSAL, NST>::run(a);
 }
 
-// Merge of the split partials, one output row per D/4 threads (4 consecutive
-// d per thread): M = max_p LSE_p, w_p = exp(LSE_p - M),
+// Merge of the split partials: M = max_p LSE_p, w_p = exp(LSE_p - M),
 // O = sum_p w_p O_p / sum_p w_p, LSE = M + ln sum_p w_p.  A row with no
 // visible key anywhere (M = -inf) gets O = 0 and LSE = -inf.
+//
+// One output row per 16 lanes, 8 consecutive d per lane at D = 128 (4 at
+// D = 64), so a 256-thread block merges 16 rows.  The partial LSEs of a row
+// are read first, kMergeUnroll at a time with independent loads; then the
+// partial outputs, again kMergeUnroll independent loads in flight per lane:
+// a merge of few rows is bound by memory latency, not bandwidth.
+constexpr int kMergeLanes = 16;   // lanes per output row
+constexpr int kMergeRows = 256 / kMergeLanes;
+constexpr int kMergeUnroll = 8;
+
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_splitkv_merge(const MergeArgs a)
 {
-    constexpr int kTpr = D / 4, kRows = 256 / kTpr;
-    const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / kTpr;
+    constexpr int kPer = D / kMergeLanes;  // d per lane: 8 or 4
+    typedef float vec __attribute__((ext_vector_type(kPer)));
+    const int64_t row = (int64_t)blockIdx.x * kMergeRows + threadIdx.x / kMergeLanes;
     if (row >= a.n_rows) return;
-    const int d0 = 4 * (threadIdx.x % kTpr);
+    const int d0 = kPer * (threadIdx.x % kMergeLanes);
     const int n = a.n_splits;
     const float *lp = a.ws_lse + row * n;
     const float *op = a.ws_o + row * n * D + d0;
+    const float ninf = -__builtin_huge_valf();
 
-    float m = -__builtin_huge_valf();
-    for (int p = 0; p < n; ++p) m = fmaxf(m, lp[p]);
-    float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float m = ninf;
+    for (int p0 = 0; p0 < n; p0 += kMergeUnroll) {
+        float v[kMergeUnroll];
+#pragma unroll
+        for (int j = 0; j < kMergeUnroll; ++j) v[j] = p0 + j < n ? lp[p0 + j] : ninf;
+#pragma unroll
+        for (int j = 0; j < kMergeUnroll; ++j) m = fmaxf(m, v[j]);
+    }
+    vec acc = {};
     float wsum = 0.0f;
-    if (m != -__builtin_huge_valf()) {
-        for (int p = 0; p < n; ++p) {
-            const float lsep = lp[p];
-            if (lsep == -__builtin_huge_valf()) continue;  // empty split: weight 0
-            const float w = expf(lsep - m);
-            wsum += w;
-            acc += w * *(const float4v *)(op + (int64_t)p * D);
+    if (m != ninf) {
+        for (int p0 = 0; p0 < n; p0 += kMergeUnroll) {
+            float w[kMergeUnroll];
+            vec o[kMergeUnroll];
+#pragma unroll
+            for (int j = 0; j < kMergeUnroll; ++j) {
+                const bool in = p0 + j < n;
+                const float l = in ? lp[p0 + j] : ninf;
+                // an empty split (LSE_p = -inf) has weight exp(-inf) = 0
+                w[j] = expf(l - m);
+                o[j] = in ? *(const vec *)(op + (int64_t)(p0 + j) * D) : vec{};
+            }
+#pragma unroll
+            for (int j = 0; j < kMergeUnroll; ++j) {
+                wsum += w[j];
+                acc += w[j] * o[j];
+            }
         }
     }
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
     // row = (b*H + h)*Lq + i  ->  O[b][i][h][:]
     const int64_t bh = row / a.Lq, i = row % a.Lq;
     const int64_t b = bh / a.H, h = bh % a.H;
-    const half4 out = __builtin_convertvector(acc * inv, half4);
-    *(half4 *)(a.o + ((b * a.Lq + i) * a.H + h) * D + d0) = out;
-    if (a.lse && d0 == 0) a.lse[row] = wsum > 0.0f ? m + logf(wsum) : -__builtin_huge_valf();
+    _Float16 *orow = a.o + ((b * a.Lq + i) * a.H + h) * D + d0;
+    const vec r = acc * inv;
+#pragma unroll
+    for (int j = 0; j < kPer; j += 4) {
+        const float4v q4 = {r[j], r[j + 1], r[j + 2], r[j + 3]};
+        *(half4 *)(orow + j) = __builtin_convertvector(q4, half4);
+    }
+    if (a.lse && d0 == 0) a.lse[row] = wsum > 0.0f ? m + logf(wsum) : ninf;
 }
 
 constexpr int kStages = 3;  // ring depth of the split kernel
@@ -325,8 +357,7 @@ int launch_split(const SplitArgs &s, const MergeArgs &mg, hipStream_t stream)
 {
     hipLaunchKernelGGL((fa_splitkv_kernel<D, CAUSAL, kStages>), dim3(s.n_items), dim3(64), 0, stream, s);
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
-    constexpr int kRows = 256 / (D / 4);
-    const int64_t blocks = (mg.n_rows + kRows - 1) / kRows;
+    const int64_t blocks = (mg.n_rows + kMergeRows - 1) / kMergeRows;
     hipLaunchKernelGGL((fa_splitkv_merge<D>), dim3((unsigned)blocks), dim3(256), 0, stream, mg);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -354,8 +385,7 @@ int launch_splitkv(const Problem &p, int n_splits, void *workspace, hipStream_t 
     const int64_t items = (int64_t)p.B * p.Hkv * n_rb * n_splits;
     if (rows > 0x7fffffff - 64 || items > 0x7fffffff) return FA_ERR_SHAPE;
     const int64_t n_rows = (int64_t)p.B * p.H * p.Lq;
-    const int kRowsMerge = 256 / (p.D / 4);
-    if ((n_rows + kRowsMerge - 1) / kRowsMerge > 0x7fffffff) return FA_ERR_SHAPE;
+    if ((n_rows + kMergeRows - 1) / kMergeRows > 0x7fffffff) return FA_ERR_SHAPE;
 
     // visible keys: all of them, or (causal) up to the last query's position
     int64_t kv_vis = p.Lk;
