@@ -50,6 +50,25 @@
  * Floating point: every score is a sum over d in ascending order of exact
  * fp16*fp16 products, in double; exp/log are the C library's double routines.
  * Compiled without -ffast-math so the summation order is the one written.
+ *
+ * Backward pass (fa_oracle_bwd): the gradients of the scalar
+ * sum_{b,i,h,d} O[b,i,h,d] * dO[b,i,h,d] with respect to Q, K and V, for
+ * equal query and key lengths.  Page "TileLang 与机器学习训练：反向传播算子优化
+ * 案例", section "算子拆分与流水线设计", splits the computation into a
+ * preprocess computing Delta from O and dO and a main kernel producing dQ,
+ * dK and dV from Q, K, V, dO, lse and Delta; the section "反向传播算子的性能
+ * 挑战" names its parts: the input gradients and the softmax-derivative
+ * adjustment.  Written out by the chain rule through the softmax, per row i
+ * of head h (K/V head hk, visible keys j):
+ *   P_ij  = softmax_j(s_ij)                  (the forward's probabilities)
+ *   dP_ij = sum_d dO[i,d] * V[j,d]
+ *   Delta_i = sum_j P_ij * dP_ij             (= sum_d O[i,d] * dO[i,d])
+ *   dS_ij = P_ij * (dP_ij - Delta_i)         (softmax derivative)
+ *   dQ[i,:]  = scale * sum_j dS_ij * K[j,:]
+ *   dK[j,:] += scale * dS_ij * Q[i,:]        (summed over i and over the
+ *   dV[j,:] += P_ij * dO[i,:]                  query heads of the group)
+ * dO is an input in binary16 bits like Q, K, V; the gradients are written
+ * in double.
  */
 #include <math.h>
 #include <pthread.h>
@@ -351,4 +370,117 @@ int fa_oracle_row_probs(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         double scale, int b, int h, int i, double *probs)
 {
     return fa_oracle_row_probs_kv(q, k, v, B, L, L, H, Hkv, D, causal, 0, scale, b, h, i, probs);
+}
+
+/* ---------------------------------------------------------------- backward */
+
+typedef struct {
+    const problem_t *p;
+    const uint16_t *dout;
+    double *dq, *dk, *dv;
+    long n_items; /* B * Hkv */
+    long next;
+    pthread_mutex_t lock;
+} bwd_job_t;
+
+static long bwd_take(bwd_job_t *job)
+{
+    pthread_mutex_lock(&job->lock);
+    long it = job->next < job->n_items ? job->next++ : -1;
+    pthread_mutex_unlock(&job->lock);
+    return it;
+}
+
+/* All gradients that involve K/V head hk of batch b: dQ of the query heads
+ * of its group, and dK, dV of hk (accumulated over those heads' rows in
+ * ascending head, then row, order -- one thread owns them, so the result
+ * does not depend on the thread count). */
+static void bwd_group(const problem_t *p, const uint16_t *dout, int b, int hk, double *dq,
+                      double *dk, double *dv, double *prob, double *dprob, double *o_row)
+{
+    const int groups = p->H / p->Hkv;
+    for (int j = 0; j < p->Lk; ++j)
+        for (int d = 0; d < p->D; ++d) {
+            dk[kv_index(p, b, j, hk, d)] = 0.0;
+            dv[kv_index(p, b, j, hk, d)] = 0.0;
+        }
+    for (int h = hk * groups; h < (hk + 1) * groups; ++h) {
+        for (int i = 0; i < p->Lq; ++i) {
+            double lse;
+            /* the forward's probabilities of row i (prob[j], j < n) */
+            attention_row(p, b, h, i, prob, o_row, &lse);
+            const int n = visible_keys(p, i);
+            /* dP_ij and Delta_i */
+            double delta = 0.0;
+            for (int j = 0; j < n; ++j) {
+                double acc = 0.0;
+                for (int d = 0; d < p->D; ++d)
+                    acc += h2d(dout[q_index(p, b, i, h, d)]) * h2d(p->v[kv_index(p, b, j, hk, d)]);
+                dprob[j] = acc;
+                delta += prob[j] * acc;
+            }
+            /* dS_ij = P_ij (dP_ij - Delta_i), kept in dprob */
+            for (int j = 0; j < n; ++j) dprob[j] = prob[j] * (dprob[j] - delta);
+            for (int d = 0; d < p->D; ++d) {
+                double acc = 0.0;
+                for (int j = 0; j < n; ++j) acc += dprob[j] * h2d(p->k[kv_index(p, b, j, hk, d)]);
+                dq[q_index(p, b, i, h, d)] = p->scale * acc;
+            }
+            for (int j = 0; j < n; ++j)
+                for (int d = 0; d < p->D; ++d) {
+                    dk[kv_index(p, b, j, hk, d)] += p->scale * dprob[j] * h2d(p->q[q_index(p, b, i, h, d)]);
+                    dv[kv_index(p, b, j, hk, d)] += prob[j] * h2d(dout[q_index(p, b, i, h, d)]);
+                }
+        }
+    }
+}
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job_t *job = (bwd_job_t *)arg;
+    const problem_t *p = job->p;
+    size_t n = (size_t)(p->Lk > 0 ? p->Lk : 1);
+    double *prob = (double *)malloc(sizeof(double) * n);
+    double *dprob = (double *)malloc(sizeof(double) * n);
+    double *o_row = (double *)malloc(sizeof(double) * (size_t)p->D);
+    long it;
+    while ((it = bwd_take(job)) >= 0)
+        bwd_group(p, job->dout, (int)(it / p->Hkv), (int)(it % p->Hkv), job->dq, job->dk, job->dv,
+                  prob, dprob, o_row);
+    free(prob);
+    free(dprob);
+    free(o_row);
+    return NULL;
+}
+
+/* Gradients of sum(O * dO) for the attention forward with sequence length
+ * L (queries = keys, mask i >= j when causal): dq [B][L][H][D], dk and dv
+ * [B][L][Hkv][D], all double.  q, k, v, dout are binary16 bits in the
+ * forward's layouts (dout like q).  Work is split over (b, K/V head) among
+ * `nthreads` threads (0 = all online cores); returns 0, or -1 on invalid
+ * sizes. */
+int fa_oracle_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                  double *dq, double *dk, double *dv, int B, int L, int H, int Hkv, int D,
+                  int causal, double scale, int nthreads)
+{
+    if (check_problem(B, L, L, H, Hkv, D)) return -1;
+    problem_t p = {q, k, v, B, L, L, H, Hkv, D, causal ? 1 : 0, 0, scale};
+    bwd_job_t job;
+    memset(&job, 0, sizeof(job));
+    job.p = &p;
+    job.dout = dout;
+    job.dq = dq;
+    job.dk = dk;
+    job.dv = dv;
+    job.n_items = (long)B * Hkv;
+    if (job.n_items <= 0 || L == 0) return 0;
+    int nt = resolve_threads(nthreads);
+    if (nt > job.n_items) nt = (int)job.n_items;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
+    pthread_mutex_init(&job.lock, NULL);
+    for (int t = 0; t < nt; ++t) pthread_create(&tid[t], NULL, bwd_worker, &job);
+    for (int t = 0; t < nt; ++t) pthread_join(tid[t], NULL);
+    pthread_mutex_destroy(&job.lock);
+    free(tid);
+    return 0;
 }

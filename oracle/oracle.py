@@ -60,6 +60,9 @@ def _bind(path: str):
     lib.fa_oracle_row_probs_kv.argtypes = ([u16p, u16p, u16p] + [c_int] * 8 +
                                            [c_double, c_int, c_int, c_int, f64p])
     lib.fa_oracle_row_probs_kv.restype = c_int
+    lib.fa_oracle_bwd.argtypes = ([u16p, u16p, u16p, u16p, f64p, f64p, f64p] + [c_int] * 6 +
+                                  [c_double, c_int])
+    lib.fa_oracle_bwd.restype = c_int
     return lib
 
 
@@ -185,6 +188,32 @@ def row_probs(q, k, v, b: int, h: int, i: int, causal: bool = False, scale: floa
     if rc:
         raise ValueError("oracle rejected the row")
     return p
+
+
+def backward(q, k, v, dout, causal: bool = False, scale: float | None = None, nthreads: int = 0,
+             lib=None):
+    """Gradients of sum(O * dout) in fp64 for equal query and key lengths.
+    q, dout [B, L, H, D], k, v [B, L, Hkv, D] (float16).  Returns
+    (dq [B,L,H,D], dk [B,L,Hkv,D], dv [B,L,Hkv,D]) as float64 arrays."""
+    lib = lib or _load()
+    q, k, v, B, Lq, Lk, H, Hkv, D = _shape(q, k, v)
+    do = _as_half_bits(dout)
+    if Lq != Lk:
+        raise ValueError("the backward oracle takes equal query and key lengths")
+    if do.shape != q.shape:
+        raise ValueError(f"dout {do.shape} must be shaped like q {q.shape}")
+    scale = default_scale(D) if scale is None else float(scale)
+    dq = np.empty((B, Lq, H, D), np.float64)
+    dk = np.empty((B, Lk, Hkv, D), np.float64)
+    dv = np.empty((B, Lk, Hkv, D), np.float64)
+    rc = lib.fa_oracle_bwd(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                           _ptr(v, ctypes.c_uint16), _ptr(do, ctypes.c_uint16),
+                           _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                           _ptr(dv, ctypes.c_double), B, Lq, H, Hkv, D, int(bool(causal)), scale,
+                           int(nthreads))
+    if rc:
+        raise ValueError("oracle rejected the problem")
+    return dq, dk, dv
 
 
 def half_to_double(bits: int, lib=None) -> float:

@@ -112,6 +112,26 @@ def make_qkv(B: int, L: int, H: int, Hkv: int, D: int, seed: int = 0, qk_mult: f
     return q, k, v
 
 
+def make_qkvdo(B: int, L: int, H: int, Hkv: int, D: int, seed: int = 0, qk_mult: float = 1.0,
+               device: str | torch.device = "cpu"):
+    """Backward-pass inputs: Q, K, V exactly as make_qkv draws them, then,
+    from the same generator, the output gradient dO [B, L, H, D] as i.i.d.
+    N(0, 1) float32 rounded to float16."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, L, H, D), generator=g, dtype=torch.float32)
+    k = torch.randn((B, L, Hkv, D), generator=g, dtype=torch.float32)
+    v = torch.randn((B, L, Hkv, D), generator=g, dtype=torch.float32)
+    do = torch.randn((B, L, H, D), generator=g, dtype=torch.float32)
+    if qk_mult != 1.0:
+        q = q * qk_mult
+        k = k * qk_mult
+    out = [t.half() for t in (q, k, v, do)]
+    if str(device) != "cpu":
+        out = [t.to(device) for t in out]
+    return tuple(out)
+
+
 def workload_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu"):
     return make_qkv(w.B, w.L, w.H, w.Hkv, w.D, seed=seed, qk_mult=w.qk_mult, device=device,
                     Lk=w.keys)
