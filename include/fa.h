@@ -166,12 +166,46 @@ FA_API int fa_splitkv_splits(int B, int Lq, int Lk, int H, int Hkv, int D, int c
  * 64 or 128, n_splits outside 1..4096) or int64 overflow. */
 FA_API long long fa_splitkv_workspace_bytes(int B, int Lq, int H, int D, int n_splits);
 
+/*
+ * fa_bwd -- attention backward pass: the gradients of sum(O * dout) with
+ * respect to q, k and v, for queries and keys of equal length L (page
+ * "TileLang 与机器学习训练：反向传播算子优化案例", section "算子拆分与流水线设计":
+ * a preprocess computing Delta from O and dO, then the gradient kernels,
+ * which consume lse and Delta).  Per row i of query head h (K/V head hk):
+ *   P_ij    = exp(s_ij - LSE[b,h,i])        s_ij as in fa_fwd, masked keys 0
+ *   Delta_i = sum_d O[b,i,h,d] * dout[b,i,h,d]
+ *   dS_ij   = P_ij * (sum_d dout[b,i,h,d] * V[b,j,hk,d] - Delta_i)
+ *   dq[b,i,h,:]  = scale * sum_j dS_ij * K[b,j,hk,:]
+ *   dk[b,j,hk,:] = scale * sum over (i, h in hk's group) of dS_ij * Q[b,i,h,:]
+ *   dv[b,j,hk,:] = sum over (i, h in hk's group) of P_ij * dout[b,i,h,:]
+ * computed with fp16 MFMA operands (P and dS rounded to fp16) and fp32
+ * accumulation; the gradients are written as fp16 (round to nearest even).
+ *
+ * q, k, v     device pointers, the forward's inputs (layouts as for fa_fwd)
+ * o           device pointer, fp16 [B][L][H][D]: the forward's output   (read)
+ * dout        device pointer, fp16 [B][L][H][D]: gradient of the output (read)
+ * lse         device pointer, fp32 [B][H][L]: the forward's LSE         (read)
+ * delta       device pointer, fp32 [B][H][L]: receives Delta        (written)
+ * dq          device pointer, fp16 [B][L][H][D]                     (written)
+ * dk, dv      device pointers, fp16 [B][L][Hkv][D]                  (written)
+ * B, L, H, Hkv, D, causal, scale, stream   as for fa_fwd.
+ *
+ * Ownership, sizes and errors as for fa_fwd; every pointer must be non-NULL
+ * (FA_ERR_NULLPTR), 16-byte aligned (lse and delta: 4-byte; FA_ERR_ALIGN),
+ * and the written buffers (delta, dq, dk, dv) must not overlap any other
+ * buffer (FA_ERR_ALIAS).  B == 0 or L == 0 returns FA_OK and launches
+ * nothing.  No atomics: results are deterministic.
+ */
+FA_API int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                  const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int L,
+                  int H, int Hkv, int D, int causal, float scale, hipStream_t stream);
+
 /* Human-readable name of an fa_status value (static storage, never NULL). */
 FA_API const char *fa_status_string(int status);
 
 /* Version of this ABI (bumped when an entry point is added or a signature or
  * a layout changes): 2 = fa_fwd, fa_fwd_kv; 3 adds fa_fwd_splitkv,
- * fa_splitkv_splits and fa_splitkv_workspace_bytes. */
+ * fa_splitkv_splits and fa_splitkv_workspace_bytes; 4 adds fa_bwd. */
 FA_API int fa_abi_version(void);
 
 #ifdef __cplusplus

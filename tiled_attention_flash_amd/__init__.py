@@ -25,7 +25,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "forward_splitkv", "fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv",
+__all__ = ["forward", "forward_splitkv", "backward", "fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv", "fa_bwd",
            "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_status_string", "library",
            "library_path", "FaError", "STATUS"]
 
@@ -71,6 +71,8 @@ def library():
     lib.fa_splitkv_splits.restype = c_int
     lib.fa_splitkv_workspace_bytes.argtypes = [c_int] * 5
     lib.fa_splitkv_workspace_bytes.restype = ctypes.c_longlong
+    lib.fa_bwd.argtypes = [vp] * 10 + [c_int] * 6 + [ctypes.c_float, vp]
+    lib.fa_bwd.restype = c_int
     lib.fa_status_string.argtypes = [c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -178,6 +180,51 @@ def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None, o
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out, lse
+
+
+def fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, L, H, Hkv, D, causal, scale,
+           stream) -> int:
+    """Direct call of the backward entry point; status returned unchanged."""
+    return int(library().fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, int(B), int(L), int(H),
+                                int(Hkv), int(D), int(bool(causal)), float(scale), stream))
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, delta=None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for the forward that produced
+    o and lse from q, k, v (equal query and key lengths), on the current
+    stream.  Output and Delta buffers are allocated with torch unless given;
+    returns (dq, dk, dv, delta)."""
+    import torch
+
+    _check_qkv(q, k, v)
+    B, L, H, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape[1] != L:
+        raise ValueError("backward takes equal query and key lengths")
+    for name, t in (("o", o), ("dout", dout)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or t.shape != q.shape or
+                not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous float16 tensor shaped like q on q's device")
+    for name, t in (("lse", lse), ("delta", delta)):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, L) or
+                              not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, L] tensor on q's device")
+    if lse is None:
+        raise ValueError("lse is required")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if delta is None else delta
+    ptrs = [t.data_ptr() or None for t in (q, k, v, o, dout, lse, delta, dq, dk, dv)]
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_bwd(*ptrs, B, L, H, Hkv, D, causal, scale, stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return dq, dk, dv, delta
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,

@@ -177,6 +177,45 @@ extern "C" int fa_fwd_splitkv(const void *q, const void *k, const void *v, void 
     return fa::launch_splitkv(p, n_splits, workspace, stream);
 }
 
+extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, float *delta, void *dq, void *dk,
+                      void *dv, int B, int L, int H, int Hkv, int D, int causal, float scale,
+                      hipStream_t stream)
+{
+    if (B < 0 || L < 0 || H < 0 || Hkv < 0 || D < 0) return FA_ERR_SHAPE;
+    if (H <= 0 || Hkv <= 0 || H % Hkv != 0) return FA_ERR_GQA;
+    if (D != 64 && D != 128) return FA_ERR_HEADDIM;
+    if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+    if (L > (1 << 30)) return FA_ERR_SHAPE;
+    const int64_t q_elems = elems4(B, L, H, D), kv_elems = elems4(B, L, Hkv, D);
+    const int64_t row_elems = elems4(B, H, L, 1);
+    if (q_elems < 0 || kv_elems < 0 || row_elems < 0 || q_elems > INT64_MAX / 4 ||
+        kv_elems > INT64_MAX / 4)
+        return FA_ERR_SHAPE;
+    if (B == 0 || L == 0) return FA_OK;
+
+    if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA_ERR_NULLPTR;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
+        misaligned(lse, 4) || misaligned(delta, 4))
+        return FA_ERR_ALIGN;
+
+    // every written buffer is disjoint from every other buffer
+    const int64_t qb = q_elems * 2, kvb = kv_elems * 2, rb = row_elems * 4;
+    const void *in[6] = {q, k, v, o, dout, lse};
+    const int64_t in_bytes[6] = {qb, kvb, kvb, qb, qb, rb};
+    void *out[4] = {delta, dq, dk, dv};
+    const int64_t out_bytes[4] = {rb, qb, kvb, kvb};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(out[i], out_bytes[i], in[j], in_bytes[j])) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(out[i], out_bytes[i], out[j], out_bytes[j])) return FA_ERR_ALIAS;
+    }
+    fa::BwdProblem p{q, k, v, o, dout, lse, delta, dq, dk, dv, B, L, H, Hkv, D, causal != 0, scale};
+    return fa::launch_backward(p, stream);
+}
+
 extern "C" const char *fa_status_string(int status)
 {
     switch (status) {
@@ -197,4 +236,4 @@ extern "C" const char *fa_status_string(int status)
     }
 }
 
-extern "C" int fa_abi_version(void) { return 3; }
+extern "C" int fa_abi_version(void) { return 4; }

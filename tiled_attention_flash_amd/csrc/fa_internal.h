@@ -31,4 +31,19 @@ int launch_forward(const Problem &p, hipStream_t stream);
 int64_t splitkv_workspace_bytes(int64_t rows_total, int64_t n_splits, int D);
 int launch_splitkv(const Problem &p, int n_splits, void *workspace, hipStream_t stream);
 
+// Validated backward problem (queries and keys equally long).
+struct BwdProblem {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    float *delta;
+    void *dq, *dk, *dv;
+    int B, L, H, Hkv, D;
+    bool causal;
+    float scale;
+};
+
+// Enqueues the backward kernels (Delta, dK/dV, dQ) on `stream`.  Returns
+// FA_OK, FA_ERR_SHAPE or FA_ERR_LAUNCH.
+int launch_backward(const BwdProblem &p, hipStream_t stream);
+
 }  // namespace fa
