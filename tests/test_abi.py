@@ -36,7 +36,8 @@ def test_library_loads_and_exports_header_symbols():
     lib = fa.library()
     names = declared_symbols()
     assert set(names) == {"fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv", "fa_splitkv_splits",
-                          "fa_splitkv_workspace_bytes", "fa_status_string", "fa_abi_version"}
+                          "fa_splitkv_workspace_bytes", "fa_bwd", "fa_status_string",
+                          "fa_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], check=True,
                          stdout=subprocess.PIPE, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -45,7 +46,7 @@ def test_library_loads_and_exports_header_symbols():
         assert hasattr(lib, n)
     # nothing beyond the declared C ABI leaks out of the library
     assert exported == set(names)
-    assert lib.fa_abi_version() == 3
+    assert lib.fa_abi_version() == 4
 
 
 def test_status_strings():
@@ -267,3 +268,38 @@ def test_splitkv_exact_workspace_size_accepted_by_validation():
     assert call_split(Lq=0, workspace=None, workspace_bytes=0) == 0
     assert call_split(B=0, workspace=None, workspace_bytes=0) == 0
     assert call_split(B=0, n_splits=5000) == 2  # still validated
+
+
+# ------------------------------------------------------------ backward ABI
+
+DO, DELTA, DQ, DK, DV = 0x70000000, 0x80000000, 0x90000000, 0xA0000000, 0xB0000000
+BWD_ARGS = dict(q=Q, k=K, v=V, o=O, dout=DO, lse=LSE, delta=DELTA, dq=DQ, dk=DK, dv=DV, B=1, L=128,
+                H=2, Hkv=2, D=64, causal=0, scale=0.125, stream=None)
+
+
+def call_bwd(**kw):
+    a = dict(BWD_ARGS)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["delta"], a["dq"],
+                     a["dk"], a["dv"], a["B"], a["L"], a["H"], a["Hkv"], a["D"], a["causal"],
+                     a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(dout=None), 1), (dict(lse=None), 1),
+    (dict(delta=None), 1), (dict(dq=None), 1), (dict(dk=None), 1), (dict(dv=None), 1),
+    (dict(L=-1), 2), (dict(L=(1 << 30) + 1), 2), (dict(H=3, Hkv=2), 3), (dict(D=96), 4),
+    (dict(scale=0.0), 5), (dict(dout=DO + 8), 6), (dict(delta=DELTA + 2), 6), (dict(dk=DK + 4), 6),
+    (dict(dq=Q), 7), (dict(dk=DV), 7), (dict(delta=LSE), 7), (dict(dv=O + 64), 7),
+    (dict(dq=DO - 1024), 7), (dict(delta=DQ + 256), 7),
+])
+def test_bwd_invalid_arguments_rejected_without_launch(kw, status):
+    assert call_bwd(**kw) == status
+
+
+def test_bwd_empty_problems_are_noops():
+    nulls = dict(q=None, k=None, v=None, o=None, dout=None, lse=None, delta=None, dq=None,
+                 dk=None, dv=None)
+    assert call_bwd(B=0, **nulls) == 0
+    assert call_bwd(L=0, **nulls) == 0
+    assert call_bwd(L=0, D=96) == 4
