@@ -204,13 +204,28 @@ def main() -> int:
     w = WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, k, v = workload_inputs(w, seed=args.seed)
+    if w.path == "backward":
+        from tiled_attention_flash_amd.inputs import make_qkvdo
+        q, k, v, do = make_qkvdo(w.B, w.L, w.H, w.Hkv, w.D, seed=args.seed, qk_mult=w.qk_mult)
+    else:
+        q, k, v = workload_inputs(w, seed=args.seed)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     o = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    if w.path == "splitkv":
+    if w.path == "backward":
+        # the forward's O and LSE are inputs of the backward, resident before timing
+        fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        dod = do.to(dev)
+        gq, gk, gv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        delta = torch.empty_like(lse)
+        n_splits = None
+
+        def step():
+            fa.backward(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dq=gq, dk=gk,
+                        dv=gv, delta=delta)
+    elif w.path == "splitkv":
         n_splits = fa.fa_splitkv_splits(w.B, w.L, w.keys, w.H, w.Hkv, w.D, w.causal, w.past_len)
         ws = torch.empty(fa.fa_splitkv_workspace_bytes(w.B, w.L, w.H, w.D, n_splits),
                          dtype=torch.uint8, device=dev)
@@ -248,7 +263,7 @@ def main() -> int:
     kernel_ms = sum(per_launch) / len(per_launch)
     ms_per_step = total_ms / args.steps
 
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    value = w.step_flops / (ms_per_step * 1e-3) / 1e12
     traffic = measured_traffic(name)
     if w.path == "splitkv":
         # decoding reads each K/V byte once and does ~1 flop per byte: HBM-bound
@@ -257,10 +272,12 @@ def main() -> int:
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                     "algorithmic_bytes": w.algorithmic_bytes}
     else:
-        achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+        achieved = w.step_flops / (kernel_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                     "traffic": traffic}
+        if w.path == "backward":
+            roofline["flops_counted"] = "2.5 x 4*B*H*L^2*D (S, dP, dV, dK, dQ), causal halved"
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -278,7 +295,8 @@ def main() -> int:
                    "causal": w.causal, "layout": "BSHD", "seed": args.seed,
                    **({"Lk": w.keys, "past_len": w.past_len} if w.keys != w.L else {}),
                    **({"entry_point": "fa_fwd_splitkv", "n_splits": n_splits}
-                      if n_splits is not None else {})},
+                      if n_splits is not None else {}),
+                   **({"entry_point": "fa_bwd"} if w.path == "backward" else {})},
         "pct_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2),
         "roofline": roofline,
         "kernel_ms_mean": round(kernel_ms, 5),
@@ -295,7 +313,7 @@ def main() -> int:
         clock["peak_at_clock_tflops"] = round(peak_at_clock, 1)
         clock["frac_at_clock"] = round(achieved / peak_at_clock, 4)
     result["clock"] = clock
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.path != "backward":
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0

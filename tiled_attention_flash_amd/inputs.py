@@ -32,7 +32,7 @@ class Workload:
     causal: bool
     qk_mult: float = 1.0  # Q and K are multiplied by this before the fp16 cast
     Lk: int | None = None  # key rows; None = L (queries and keys equally long)
-    path: str = "forward"  # entry point that computes it: "forward" or "splitkv"
+    path: str = "forward"  # entry point: "forward", "splitkv" or "backward"
 
     @property
     def Lq(self) -> int:
@@ -63,6 +63,13 @@ class Workload:
         return 4.0 * self.B * self.H * self.D * pairs
 
     @property
+    def step_flops(self) -> float:
+        """Flops of one step of the workload's path: the forward's, or for
+        the backward its five products (S recomputed, dP, dV, dK, dQ) of
+        2*D flops per (query, key) pair: 2.5 times the forward's."""
+        return 2.5 * self.flops if self.path == "backward" else self.flops
+
+    @property
     def algorithmic_bytes(self) -> int:
         """Each tensor moved once: Q and O (fp16), K and V (fp16), LSE (fp32)."""
         qo = 2 * self.B * self.L * self.H * self.D * 2
@@ -88,6 +95,15 @@ WORKLOADS = {
         "decode-b8-h32-kv8-q1-k32768-d128-causal", 8, 32, 8, 1, 128, True, 1.0, 32768, "splitkv"),
     "decode-b8-h32-q1-k4096-d128-causal": Workload(
         "decode-b8-h32-q1-k4096-d128-causal", 8, 32, 32, 1, 128, True, 1.0, 4096, "splitkv"),
+    # backward: the backward page's workload (LLaMA-7B head shape) and the long shape
+    "bwd-b8-h32-L1024-d64": Workload("bwd-b8-h32-L1024-d64", 8, 32, 32, 1024, 64, False,
+                                     path="backward"),
+    "bwd-b8-h32-L1024-d64-causal": Workload("bwd-b8-h32-L1024-d64-causal", 8, 32, 32, 1024, 64,
+                                            True, path="backward"),
+    "bwd-b8-h32-L4096-d128": Workload("bwd-b8-h32-L4096-d128", 8, 32, 32, 4096, 128, False,
+                                      path="backward"),
+    "bwd-b8-h32-L4096-d128-causal": Workload("bwd-b8-h32-L4096-d128-causal", 8, 32, 32, 4096, 128,
+                                             True, path="backward"),
 }
 
 HEADLINE = "mha-b8-h32-L4096-d128"
