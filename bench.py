@@ -29,7 +29,7 @@ PEAK_FP16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0  # HBM3E, published
 CSRC = os.path.join(ROOT, "tiled_attention_flash_amd", "csrc")
 KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("fa_device.h", "fa_fwd_kernel.hip",
-                                                 "fa_splitkv_kernel.hip")]
+                                                 "fa_splitkv_kernel.hip", "fa_bwd_kernel.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
