@@ -179,8 +179,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: the forward pass here is a single-GPU kernel "
-              "and no multi-GPU path is built (see DESIGN.md for how it would shard).",
+        print("bench.py runs on exactly one GPU: the attention kernels here work on one GPU's "
+              "share of a problem and no multi-GPU path is built.",
               file=sys.stderr)
         return 2
 

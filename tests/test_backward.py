@@ -4,10 +4,10 @@ The GPU path runs the forward (fa_fwd) and then the backward on the same
 seeded inputs; the oracle computes the exact gradients of sum(O * dO) from
 Q, K, V and dO alone.
 
-Bar, per gradient tensor G in {dQ, dK, dV} (derived in the design doc from the
-arithmetic: fp16 operands P and dS carry a relative rounding of 2^-11 into
-fp32 sums, and the fp16 result another 2^-12, so errors are a few 1e-4 of
-the gradient's own scale):
+Bar, per gradient tensor G in {dQ, dK, dV}, derived from the arithmetic:
+fp16 operands P and dS carry a relative rounding of 2^-11 into fp32 sums,
+and the fp16 result another 2^-12, so errors are a few 1e-4 of the
+gradient's own scale:
     max |G_gpu - G_ref|  <= 1e-2 * max |G_ref|
     mean |G_gpu - G_ref| <= 2e-3 * mean |G_ref|
 and every gradient finite.

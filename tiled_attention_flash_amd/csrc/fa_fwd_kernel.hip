@@ -43,11 +43,14 @@
 // * Software pipeline over score blocks of 32 keys: while the matrix unit
 //   computes S of block u+1, the vector ALU exponentiates block u; P.V of
 //   block u then runs beside the row maximum of block u+1.
-// * Online softmax with a lazy rescale: the reference maximum of a row is
-//   raised (and O, l rescaled) only when some row of the wavefront sees its
-//   maximum grow by more than 2^8 in the exp2 domain; otherwise the stale
-//   maximum keeps every probability <= 256 (well inside fp16's range) and the
-//   final O / l and LSE are unchanged.
+// * Online softmax against a reference maximum: block 0 sets each row's
+//   reference to its exact maximum (a row that sees any key sees key 0).
+//   Later blocks are exponentiated against the current reference with no
+//   row maximum of their own; a block whose fp16 probabilities sum to 2^15
+//   or more in some lane (an overflow to inf included) is recomputed after
+//   the reference is raised to the block's maximum and O, l are rescaled.
+//   Kept probabilities stay below 2^15, relative to a weight of 1 that the
+//   row already holds, and the final O / l and LSE are unchanged.
 // * Causal: tiles past the work item's last query are never visited; the
 //   mask code runs only on blocks that straddle a wavefront's diagonal (or
 //   hold the ragged end of the sequence).  Blocks past a wavefront's diagonal
