@@ -69,6 +69,12 @@
  *   dV[j,:] += P_ij * dO[i,:]                  query heads of the group)
  * dO is an input in binary16 bits like Q, K, V; the gradients are written
  * in double.
+ *
+ * FP8 inputs (fa_oracle_fwd_fp8, fa_oracle_rows_fp8): the same forward on
+ * E4M3-coded Q, K, V with one descale factor per tensor, plus an optional
+ * per-element error bound for implementations that round the probabilities
+ * before the weighted sum; the section at the end of this file says which
+ * passage it follows.
  */
 #include <math.h>
 #include <pthread.h>
@@ -482,5 +488,244 @@ int fa_oracle_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
     for (int t = 0; t < nt; ++t) pthread_join(tid[t], NULL);
     pthread_mutex_destroy(&job.lock);
     free(tid);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- fp8 */
+
+/* Forward with 8-bit floating-point inputs.  Page "TileLang性能分析报告：H100上
+ * FlashAttention吞吐量达1.2PFlops", section "生产环境部署建议", item 1, names
+ * FP8 mixed precision for this kernel and gives no further detail.  Read
+ * here as: Q, K, V are stored as OCP FP8 E4M3 codes, each tensor with one
+ * descale factor, so the value of a stored code c of Q is q_descale * e4m3(c)
+ * (likewise K, V); attention is then the plain definition above on those
+ * values.  O and the log-sum-exp are written in double.
+ *
+ * E4M3 (the OCP 8-bit format "E4M3", also called e4m3fn): 1 sign bit,
+ * 4 exponent bits with bias 7, 3 fraction bits; no infinities.
+ *   exponent 0                 -> (-1)^s * 2^-6 * (frac / 8)   (subnormal)
+ *   exponent 15, fraction 7    -> NaN
+ *   otherwise                  -> (-1)^s * 2^(e-7) * (1 + frac / 8)
+ * The largest finite magnitude is 448.                                    */
+double fa_oracle_e4m3_to_double(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 0xf;
+    int frac = c & 7;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)frac, -9); /* 2^-6 * frac / 2^3 */
+    else if (e == 15 && frac == 7)
+        mag = NAN;
+    else
+        mag = ldexp(1.0 + (double)frac / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+typedef struct {
+    const uint8_t *q, *k, *v;
+    int B, Lq, Lk, H, Hkv, D, causal, past_len;
+    double scale, qd, kd, vd; /* score scale; the three descales */
+    /* rounding model of the probabilities for the error bound (see
+     * fp8_row): relative error above `floor`, absolute error below it */
+    double b_rel, b_floor, b_abs;
+} problem8_t;
+
+static double g_e4m3[256];
+static pthread_once_t g_e4m3_once = PTHREAD_ONCE_INIT;
+
+static void fill_e4m3_table(void)
+{
+    for (int c = 0; c < 256; ++c) g_e4m3[c] = fa_oracle_e4m3_to_double((uint8_t)c);
+}
+
+static size_t q8_index(const problem8_t *p, int b, int i, int h, int d)
+{
+    return (((size_t)b * p->Lq + i) * p->H + h) * p->D + d;
+}
+
+static size_t kv8_index(const problem8_t *p, int b, int j, int hk, int d)
+{
+    return (((size_t)b * p->Lk + j) * p->Hkv + hk) * p->D + d;
+}
+
+static int visible_keys8(const problem8_t *p, int i)
+{
+    if (!p->causal) return p->Lk;
+    long n = (long)i + p->past_len + 1;
+    return n < 0 ? 0 : (n > p->Lk ? p->Lk : (int)n);
+}
+
+/* One output row on the decoded values (the same three steps as
+ * attention_row):
+ *   s_j = scale * sum_d (qd * Q[i,d]) * (kd * K[j,d])
+ *   w_j = exp(s_j - max s),  Z = sum_j w_j
+ *   O_d = sum_j (w_j / Z) * (vd * V[j,d]),   LSE = max s + ln Z
+ * and, when bound_row is given, for every d
+ *   bound_d = sum_j e_j * |vd * V[j,d]| / Z,
+ *   e_j = b_rel * w_j            if w_j >= b_floor
+ *         min(w_j, b_abs)        otherwise,
+ * the largest change of O_d when every weight w_j (the maximum's weight is 1)
+ * is replaced by a rounded value within e_j of it while the denominator Z
+ * stays exact.  It is the error model of an implementation that rounds the
+ * probabilities to a format with relative precision b_rel down to b_floor
+ * and a fixed spacing below it.  A row with no visible key: O = 0,
+ * LSE = -inf, bound 0. */
+static void fp8_row(const problem8_t *p, int b, int h, int i, double *s, double *o_row,
+                    double *lse_out, double *bound_row)
+{
+    int groups = p->H / p->Hkv;
+    int hk = h / groups;
+    int n = visible_keys8(p, i);
+    if (n == 0) {
+        for (int d = 0; d < p->D; ++d) {
+            o_row[d] = 0.0;
+            if (bound_row) bound_row[d] = 0.0;
+        }
+        *lse_out = -INFINITY;
+        return;
+    }
+    for (int j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < p->D; ++d)
+            dot += (p->qd * g_e4m3[p->q[q8_index(p, b, i, h, d)]]) *
+                   (p->kd * g_e4m3[p->k[kv8_index(p, b, j, hk, d)]]);
+        s[j] = p->scale * dot;
+    }
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j)
+        if (s[j] > m) m = s[j];
+    double z = 0.0;
+    for (int j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - m);
+        z += s[j];
+    }
+    for (int d = 0; d < p->D; ++d) {
+        double acc = 0.0, err = 0.0;
+        for (int j = 0; j < n; ++j) {
+            double val = p->vd * g_e4m3[p->v[kv8_index(p, b, j, hk, d)]];
+            acc += s[j] * val;
+            if (bound_row) {
+                double e = s[j] >= p->b_floor ? p->b_rel * s[j] : (s[j] < p->b_abs ? s[j] : p->b_abs);
+                err += e * fabs(val);
+            }
+        }
+        o_row[d] = acc / z;
+        if (bound_row) bound_row[d] = err / z;
+    }
+    *lse_out = m + log(z);
+}
+
+typedef struct {
+    const problem8_t *p;
+    double *o, *lse, *bound;                 /* full mode */
+    const int64_t *rows;                     /* rows mode: triples (b, h, i) */
+    double *o_rows, *lse_rows, *bound_rows;
+    long n_items, next;
+    int rows_mode;
+    pthread_mutex_t lock;
+} job8_t;
+
+static void *fp8_worker(void *arg)
+{
+    job8_t *job = (job8_t *)arg;
+    const problem8_t *p = job->p;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(p->Lk > 0 ? p->Lk : 1));
+    long chunks = (p->Lq + ROW_CHUNK - 1) / ROW_CHUNK;
+    for (;;) {
+        pthread_mutex_lock(&job->lock);
+        long it = job->next < job->n_items ? job->next++ : -1;
+        pthread_mutex_unlock(&job->lock);
+        if (it < 0) break;
+        if (job->rows_mode) {
+            const int64_t *r = job->rows + 3 * it;
+            fp8_row(p, (int)r[0], (int)r[1], (int)r[2], s, job->o_rows + (size_t)it * p->D,
+                    job->lse_rows + it, job->bound_rows ? job->bound_rows + (size_t)it * p->D : NULL);
+        } else {
+            long bh = it / chunks, c = it % chunks;
+            int b = (int)(bh / p->H), h = (int)(bh % p->H);
+            int i_end = (int)((c + 1) * ROW_CHUNK < p->Lq ? (c + 1) * ROW_CHUNK : p->Lq);
+            for (int i = (int)(c * ROW_CHUNK); i < i_end; ++i)
+                fp8_row(p, b, h, i, s, job->o + q8_index(p, b, i, h, 0),
+                        job->lse + ((size_t)b * p->H + h) * p->Lq + i,
+                        job->bound ? job->bound + q8_index(p, b, i, h, 0) : NULL);
+        }
+    }
+    free(s);
+    return NULL;
+}
+
+static void run_pool8(job8_t *job, int nthreads)
+{
+    int n = resolve_threads(nthreads);
+    if (n > job->n_items) n = (int)(job->n_items > 0 ? job->n_items : 1);
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n);
+    pthread_mutex_init(&job->lock, NULL);
+    job->next = 0;
+    for (int t = 0; t < n; ++t) pthread_create(&tid[t], NULL, fp8_worker, job);
+    for (int t = 0; t < n; ++t) pthread_join(tid[t], NULL);
+    pthread_mutex_destroy(&job->lock);
+    free(tid);
+}
+
+static int check_problem8(int B, int Lq, int Lk, int H, int Hkv, int D)
+{
+    pthread_once(&g_e4m3_once, fill_e4m3_table);
+    if (B < 0 || Lq < 0 || Lk < 0 || H <= 0 || Hkv <= 0 || D <= 0) return -1;
+    if (H % Hkv != 0) return -1;
+    return 0;
+}
+
+/* Whole fp8 forward: q [B][Lq][H][D], k, v [B][Lk][Hkv][D] E4M3 codes;
+ * o [B][Lq][H][D] and bound (same shape, may be NULL) and lse [B][H][Lq]
+ * (may be NULL) in double.  Mask and past_len as fa_oracle_fwd_kv. */
+int fa_oracle_fwd_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v, double *o,
+                      double *lse, double *bound, int B, int Lq, int Lk, int H, int Hkv, int D,
+                      int causal, int past_len, double scale, double q_descale, double k_descale,
+                      double v_descale, double b_rel, double b_floor, double b_abs, int nthreads)
+{
+    if (check_problem8(B, Lq, Lk, H, Hkv, D)) return -1;
+    problem8_t p = {q, k, v, B, Lq, Lk, H, Hkv, D, causal ? 1 : 0, past_len, scale,
+                    q_descale, k_descale, v_descale, b_rel, b_floor, b_abs};
+    double *lse_buf = lse;
+    if (!lse_buf) lse_buf = (double *)malloc(sizeof(double) * ((size_t)B * H * Lq + 1));
+    job8_t job;
+    memset(&job, 0, sizeof(job));
+    job.p = &p;
+    job.o = o;
+    job.lse = lse_buf;
+    job.bound = bound;
+    job.n_items = (long)B * H * ((Lq + ROW_CHUNK - 1) / ROW_CHUNK);
+    if (job.n_items > 0) run_pool8(&job, nthreads);
+    if (!lse) free(lse_buf);
+    return 0;
+}
+
+/* Selected rows of the fp8 forward: rows holds n_rows triples (b, h, i);
+ * o_rows and bound_rows (may be NULL) are [n_rows][D], lse_rows [n_rows]. */
+int fa_oracle_rows_fp8(const uint8_t *q, const uint8_t *k, const uint8_t *v, int B, int Lq,
+                       int Lk, int H, int Hkv, int D, int causal, int past_len, double scale,
+                       double q_descale, double k_descale, double v_descale, double b_rel,
+                       double b_floor, double b_abs, const int64_t *rows, long n_rows,
+                       double *o_rows, double *lse_rows, double *bound_rows, int nthreads)
+{
+    if (check_problem8(B, Lq, Lk, H, Hkv, D)) return -1;
+    for (long r = 0; r < n_rows; ++r) {
+        const int64_t *t = rows + 3 * r;
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= Lq)
+            return -1;
+    }
+    problem8_t p = {q, k, v, B, Lq, Lk, H, Hkv, D, causal ? 1 : 0, past_len, scale,
+                    q_descale, k_descale, v_descale, b_rel, b_floor, b_abs};
+    job8_t job;
+    memset(&job, 0, sizeof(job));
+    job.p = &p;
+    job.rows_mode = 1;
+    job.rows = rows;
+    job.o_rows = o_rows;
+    job.lse_rows = lse_rows;
+    job.bound_rows = bound_rows;
+    job.n_items = n_rows;
+    if (n_rows > 0) run_pool8(&job, nthreads);
     return 0;
 }

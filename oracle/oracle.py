@@ -63,6 +63,15 @@ def _bind(path: str):
     lib.fa_oracle_bwd.argtypes = ([u16p, u16p, u16p, u16p, f64p, f64p, f64p] + [c_int] * 6 +
                                   [c_double, c_int])
     lib.fa_oracle_bwd.restype = c_int
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.fa_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.fa_oracle_e4m3_to_double.restype = c_double
+    lib.fa_oracle_fwd_fp8.argtypes = ([u8p, u8p, u8p, f64p, f64p, f64p] + [c_int] * 8 +
+                                      [c_double] * 7 + [c_int])
+    lib.fa_oracle_fwd_fp8.restype = c_int
+    lib.fa_oracle_rows_fp8.argtypes = ([u8p, u8p, u8p] + [c_int] * 8 + [c_double] * 7 +
+                                       [i64p, c_long, f64p, f64p, f64p, c_int])
+    lib.fa_oracle_rows_fp8.restype = c_int
     return lib
 
 
@@ -214,6 +223,95 @@ def backward(q, k, v, dout, causal: bool = False, scale: float | None = None, nt
     if rc:
         raise ValueError("oracle rejected the problem")
     return dq, dk, dv
+
+
+def _as_fp8_codes(x) -> np.ndarray:
+    """E4M3 codes (torch float8_e4m3fn/uint8 tensor or uint8 array) ->
+    contiguous uint8 numpy array; only the bytes are taken."""
+    if hasattr(x, "detach"):
+        x = x.detach()
+        if x.device.type != "cpu":
+            raise ValueError("oracle inputs must live in host memory")
+        x = x.contiguous().view(dtype=__import__("torch").uint8).numpy()
+    a = np.ascontiguousarray(x)
+    if a.dtype != np.uint8:
+        raise TypeError(f"fp8 oracle inputs must be E4M3 bytes, got {a.dtype}")
+    return a
+
+
+def _shape8(q, k, v):
+    q, k, v = _as_fp8_codes(q), _as_fp8_codes(k), _as_fp8_codes(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D BSHD")
+    B, Lq, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError(f"H={H} is not a multiple of Hkv={Hkv}")
+    return q, k, v, B, Lq, Lk, H, Hkv, D
+
+
+def forward_fp8(q, k, v, descale=(1.0, 1.0, 1.0), causal: bool = False,
+                scale: float | None = None, past_len: int | None = None, bound_model=None,
+                nthreads: int = 0, lib=None):
+    """fp8 forward in fp64 on the decoded values descale * e4m3(code).
+    q [B,Lq,H,D], k/v [B,Lk,Hkv,D] E4M3 codes; descale = (q, k, v) factors.
+    Returns (o [B,Lq,H,D], lse [B,H,Lq], bound [B,Lq,H,D] or None): bound is
+    the largest change of O that rounding the probabilities under
+    ``bound_model`` = (rel, floor, abs) can cause (see fa_oracle.c)."""
+    lib = lib or _load()
+    q, k, v, B, Lq, Lk, H, Hkv, D = _shape8(q, k, v)
+    scale = default_scale(D) if scale is None else float(scale)
+    past = default_past_len(Lq, Lk) if past_len is None else int(past_len)
+    o = np.empty((B, Lq, H, D), np.float64)
+    lse = np.empty((B, H, Lq), np.float64)
+    bound = np.empty((B, Lq, H, D), np.float64) if bound_model is not None else None
+    rel, floor, ab = bound_model if bound_model is not None else (0.0, 0.0, 0.0)
+    u8 = ctypes.c_uint8
+    rc = lib.fa_oracle_fwd_fp8(_ptr(q, u8), _ptr(k, u8), _ptr(v, u8), _ptr(o, ctypes.c_double),
+                               _ptr(lse, ctypes.c_double),
+                               _ptr(bound, ctypes.c_double) if bound is not None else None,
+                               B, Lq, Lk, H, Hkv, D, int(bool(causal)), past, scale,
+                               float(descale[0]), float(descale[1]), float(descale[2]),
+                               float(rel), float(floor), float(ab), int(nthreads))
+    if rc:
+        raise ValueError("oracle rejected the problem")
+    return o, lse, bound
+
+
+def rows_fp8(q, k, v, row_ids, descale=(1.0, 1.0, 1.0), causal: bool = False,
+             scale: float | None = None, past_len: int | None = None, bound_model=None,
+             nthreads: int = 0, lib=None):
+    """Selected rows of forward_fp8: row_ids [n, 3] of (b, h, i).
+    Returns (o_rows [n, D], lse_rows [n], bound_rows [n, D] or None)."""
+    lib = lib or _load()
+    q, k, v, B, Lq, Lk, H, Hkv, D = _shape8(q, k, v)
+    scale = default_scale(D) if scale is None else float(scale)
+    past = default_past_len(Lq, Lk) if past_len is None else int(past_len)
+    r = np.ascontiguousarray(np.asarray(row_ids, dtype=np.int64).reshape(-1, 3))
+    n = r.shape[0]
+    o = np.empty((n, D), np.float64)
+    lse = np.empty((n,), np.float64)
+    bound = np.empty((n, D), np.float64) if bound_model is not None else None
+    rel, floor, ab = bound_model if bound_model is not None else (0.0, 0.0, 0.0)
+    u8 = ctypes.c_uint8
+    rc = lib.fa_oracle_rows_fp8(_ptr(q, u8), _ptr(k, u8), _ptr(v, u8), B, Lq, Lk, H, Hkv, D,
+                                int(bool(causal)), past, scale, float(descale[0]),
+                                float(descale[1]), float(descale[2]), float(rel), float(floor),
+                                float(ab), _ptr(r, ctypes.c_int64), n, _ptr(o, ctypes.c_double),
+                                _ptr(lse, ctypes.c_double),
+                                _ptr(bound, ctypes.c_double) if bound is not None else None,
+                                int(nthreads))
+    if rc:
+        raise ValueError("oracle rejected the rows")
+    return o, lse, bound
+
+
+def e4m3_to_double(code: int, lib=None) -> float:
+    """The oracle's own E4M3 decoder, exposed so it can be pinned."""
+    lib = lib or _load()
+    return float(lib.fa_oracle_e4m3_to_double(int(code) & 0xFF))
 
 
 def half_to_double(bits: int, lib=None) -> float:

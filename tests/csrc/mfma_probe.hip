@@ -3,7 +3,11 @@
 // them against a matrix product computed on the host:
 //   * v_mfma_f32_32x32x16_f16: what each lane holds of A, B and the result;
 //   * v_permlane32_swap: the two results for the same value given twice;
-//   * fp32 -> fp16 packed conversion: rounding mode.
+//   * fp32 -> fp16 packed conversion: rounding mode;
+//   * v_mfma_f32_32x32x64_f8f6f4 (fp8 e4m3 operands): which A byte meets
+//     which B byte, the result layout, the decoding of every fp8 code;
+//   * ds_read_b64_tr_b8: which LDS bytes each lane receives;
+//   * fp32 -> fp8 e4m3 packed conversion: rounding and byte placement.
 // Test support only; not part of libfa.so.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -12,6 +16,8 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float float2v __attribute__((ext_vector_type(2)));
+typedef int int8v __attribute__((ext_vector_type(8)));
+typedef int int2v __attribute__((ext_vector_type(2)));
 
 #define PROBE_API extern "C" __attribute__((visibility("default")))
 
@@ -64,5 +70,71 @@ PROBE_API int probe_cvt_f16(const void *x, void *y, int n, hipStream_t s)
     int pairs = n / 2;
     hipLaunchKernelGGL(cvt_kernel, dim3((pairs + 255) / 256), dim3(256), 0, s, (const float *)x,
                        (_Float16 *)y, n);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// a, b: [64 lanes][32 fp8 bytes] as the lanes' operand registers; c: [64][16].
+// scaled != 0: the scaled form with unit (E8M0 127) scales on both operands.
+__global__ void mfma_f8_kernel(const int8v *a, const int8v *b, floatx16 *c, int scaled)
+{
+    int l = threadIdx.x;
+    floatx16 acc = {};
+    if (scaled)
+        c[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], acc, 0, 0, 0, 127, 0, 127);
+    else
+        c[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], acc, 0, 0, 0, 0, 0, 0);
+}
+
+// LDS[0..1023] = src; lane l reads 8 bytes with ds_read_b64_tr_b8 at byte
+// offset addr[l] (a multiple of 8, at most 1016: checked on the host).
+__global__ void tr8_kernel(const int *src, const int *addr, int2v *out)
+{
+    __shared__ int lds[256];
+    int l = threadIdx.x;
+    for (int i = l; i < 256; i += 64) lds[i] = src[i];
+    __syncthreads();
+    typedef __attribute__((address_space(3))) int2v lds_int2v;
+    lds_int2v *p = (lds_int2v *)((__attribute__((address_space(3))) char *)lds + addr[l]);
+    out[l] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(p);
+}
+
+// y[4i..4i+3]: x[4i], x[4i+1] packed into the low half of a dword and
+// x[4i+2], x[4i+3] into its high half.
+__global__ void cvt_fp8_kernel(const float *x, int *y, int n4)
+{
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n4) {
+        int r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i], x[4 * i + 1], 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i + 2], x[4 * i + 3], r, true);
+        y[i] = r;
+    }
+}
+
+PROBE_API int probe_mfma_32x32x64_f8(const void *a, const void *b, void *c, int scaled, hipStream_t s)
+{
+    hipLaunchKernelGGL(mfma_f8_kernel, dim3(1), dim3(64), 0, s, (const int8v *)a, (const int8v *)b,
+                       (floatx16 *)c, scaled);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// src: 1024 bytes (device); addr: 64 ints (host and device copies: the host
+// copy is checked); out: 64 x 8 bytes.
+PROBE_API int probe_ds_read_tr8(const void *src, const int *addr_host, const void *addr_dev, void *out,
+                                hipStream_t s)
+{
+    for (int l = 0; l < 64; ++l)
+        if (addr_host[l] < 0 || addr_host[l] > 1016 || (addr_host[l] & 7)) return 2;
+    hipLaunchKernelGGL(tr8_kernel, dim3(1), dim3(64), 0, s, (const int *)src, (const int *)addr_dev,
+                       (int2v *)out);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// n must be a positive multiple of 4; x: n floats, y: n bytes.
+PROBE_API int probe_cvt_fp8(const void *x, void *y, int n, hipStream_t s)
+{
+    if (n <= 0 || (n & 3)) return 2;
+    int n4 = n / 4;
+    hipLaunchKernelGGL(cvt_fp8_kernel, dim3((n4 + 255) / 256), dim3(256), 0, s, (const float *)x,
+                       (int *)y, n4);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -12,6 +12,12 @@ softmax's logit range; finally all three are
 rounded to float16 (round-to-nearest-even).  The same float16 tensors go to the
 oracle (host) and to the GPU.  Layout is BSHD, contiguous.  The scale is
 1/sqrt(D), the value the TileLang AMD page sets up at kernel entry.
+
+FP8 workloads draw Q, K, V the same way (float32, before any rounding) and
+store each tensor as OCP E4M3 codes with one descale factor per tensor:
+descale = max|x| / 448 (448 is E4M3's largest finite value), rounded to
+float32, and code = E4M3(x / descale) by torch's float8_e4m3fn cast
+(round-to-nearest-even), the quotient clamped to +-448 first.
 """
 from __future__ import annotations
 
@@ -32,7 +38,7 @@ class Workload:
     causal: bool
     qk_mult: float = 1.0  # Q and K are multiplied by this before the fp16 cast
     Lk: int | None = None  # key rows; None = L (queries and keys equally long)
-    path: str = "forward"  # entry point: "forward", "splitkv" or "backward"
+    path: str = "forward"  # entry point: "forward", "splitkv", "backward" or "fp8"
 
     @property
     def Lq(self) -> int:
@@ -71,10 +77,12 @@ class Workload:
 
     @property
     def algorithmic_bytes(self) -> int:
-        """Each tensor moved once: Q and O (fp16), K and V (fp16), LSE (fp32)."""
-        qo = 2 * self.B * self.L * self.H * self.D * 2
-        kv = 2 * self.B * self.keys * self.Hkv * self.D * 2
-        return qo + kv + self.B * self.H * self.L * 4
+        """Each tensor moved once: Q and O (fp16), K and V (fp16), LSE (fp32);
+        with fp8 inputs Q, K, V take one byte per element."""
+        ein = 1 if self.path == "fp8" else 2
+        q = self.B * self.L * self.H * self.D
+        kv = 2 * self.B * self.keys * self.Hkv * self.D * ein
+        return q * ein + q * 2 + kv + self.B * self.H * self.L * 4
 
 
 # The workloads the method is measured on (B, H, Hkv, L, D, causal[, qk_mult, Lk]).
@@ -104,9 +112,16 @@ WORKLOADS = {
                                       path="backward"),
     "bwd-b8-h32-L4096-d128-causal": Workload("bwd-b8-h32-L4096-d128-causal", 8, 32, 32, 4096, 128,
                                              True, path="backward"),
+    # fp8 (E4M3) inputs, fp16 output
+    "fp8-mha-b8-h32-L4096-d128": Workload("fp8-mha-b8-h32-L4096-d128", 8, 32, 32, 4096, 128, False,
+                                          path="fp8"),
+    "fp8-mha-b8-h32-L4096-d128-causal": Workload("fp8-mha-b8-h32-L4096-d128-causal", 8, 32, 32,
+                                                 4096, 128, True, path="fp8"),
 }
 
 HEADLINE = "mha-b8-h32-L4096-d128"
+
+E4M3_MAX = 448.0
 
 
 def make_qkv(B: int, L: int, H: int, Hkv: int, D: int, seed: int = 0, qk_mult: float = 1.0,
@@ -148,6 +163,37 @@ def make_qkvdo(B: int, L: int, H: int, Hkv: int, D: int, seed: int = 0, qk_mult:
     return tuple(out)
 
 
+def _to_e4m3(x: torch.Tensor):
+    """float32 tensor -> (E4M3 codes as uint8, float32 descale) per the recipe."""
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    descale = float(torch.tensor(amax / E4M3_MAX if amax > 0 else 1.0, dtype=torch.float32))
+    codes = (x / descale).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, descale
+
+
+def make_qkv_fp8(B: int, L: int, H: int, Hkv: int, D: int, seed: int = 0, qk_mult: float = 1.0,
+                 device: str | torch.device = "cpu", Lk: int | None = None):
+    """Seeded fp8 Q, K, V: the float32 draws of make_qkv (same generator and
+    order, times qk_mult for Q and K), stored as E4M3 codes (uint8 tensors,
+    BSHD) with one descale per tensor.  Returns (q8, k8, v8, (qd, kd, vd))."""
+    Lk = L if Lk is None else Lk
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, L, H, D), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Lk, Hkv, D), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Lk, Hkv, D), generator=g, dtype=torch.float32)
+    if qk_mult != 1.0:
+        q = q * qk_mult
+        k = k * qk_mult
+    (q8, qd), (k8, kd), (v8, vd) = _to_e4m3(q), _to_e4m3(k), _to_e4m3(v)
+    if str(device) != "cpu":
+        q8, k8, v8 = q8.to(device), k8.to(device), v8.to(device)
+    return q8, k8, v8, (qd, kd, vd)
+
+
 def workload_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu"):
+    if w.path == "fp8":
+        return make_qkv_fp8(w.B, w.L, w.H, w.Hkv, w.D, seed=seed, qk_mult=w.qk_mult,
+                            device=device, Lk=w.keys)
     return make_qkv(w.B, w.L, w.H, w.Hkv, w.D, seed=seed, qk_mult=w.qk_mult, device=device,
                     Lk=w.keys)
