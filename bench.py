@@ -4,7 +4,9 @@
 
 One step = one fa_fwd call (the whole forward: work decomposition, Q/K/V
 tiles, both products, online softmax, normalisation, O and LSE stores) over
-the workload's seeded synthetic inputs, already resident in HBM.  Prints one
+the workload's seeded synthetic inputs, already resident in HBM; decoding
+workloads step through fa_fwd_splitkv, backward workloads through fa_bwd
+(after an untimed forward), fp8 workloads through fa_fwd_fp8.  Prints one
 JSON line on stdout; extra detail goes to stderr.
 
 Default workload: B=8, H=32, L=4096, D=128, non-causal -- the shape the
@@ -26,10 +28,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·L²·D, causal halved) + % of MFMA FP16 peak"
 PEAK_FP16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
+PEAK_FP8_TFLOPS = 5033.2  # dense E4M3: twice the fp16 rate
 PEAK_HBM_GBS = 8000.0  # HBM3E, published
 CSRC = os.path.join(ROOT, "tiled_attention_flash_amd", "csrc")
 KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("fa_device.h", "fa_fwd_kernel.hip",
-                                                 "fa_splitkv_kernel.hip", "fa_bwd_kernel.hip")]
+                                                 "fa_fwd_fp8_kernel.hip", "fa_splitkv_kernel.hip",
+                                                 "fa_bwd_kernel.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -129,7 +133,7 @@ def cpu_threads() -> int:
     return max(1, min(16, n))
 
 
-def cpu_baseline(w, q, k, v, target_s: float):
+def cpu_baseline(w, q, k, v, target_s: float, descale=None):
     """The fp64 oracle timed on the host on a bounded sample of the same
     workload: whole output rows, the first ones of every (b, h) in turn."""
     import numpy as np
@@ -150,14 +154,22 @@ def cpu_baseline(w, q, k, v, target_s: float):
             return 4.0 * w.keys * w.D * len(ids)
         return float(sum(4.0 * min(w.keys, int(i) + w.past_len + 1) * w.D for i in ids[:, 2]))
 
+    def run(ids):
+        if descale is not None:
+            oracle.rows_fp8(q, k, v, ids, descale, causal=w.causal, scale=w.scale,
+                            past_len=w.past_len, nthreads=threads)
+        else:
+            oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads,
+                        past_len=w.past_len)
+
     ids = row_ids(threads * 8)
     t0 = time.perf_counter()
-    oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads, past_len=w.past_len)
+    run(ids)
     probe = time.perf_counter() - t0
     n = int(max(threads, min(2_000_000, len(ids) * target_s / max(probe, 1e-6))))
     ids = row_ids(n)
     t0 = time.perf_counter()
-    oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale, nthreads=threads, past_len=w.past_len)
+    run(ids)
     dt = time.perf_counter() - t0
     return {"value": flops(ids) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
@@ -207,10 +219,13 @@ def main() -> int:
     if w.path == "backward":
         from tiled_attention_flash_amd.inputs import make_qkvdo
         q, k, v, do = make_qkvdo(w.B, w.L, w.H, w.Hkv, w.D, seed=args.seed, qk_mult=w.qk_mult)
+    elif w.path == "fp8":
+        q, k, v, descale = workload_inputs(w, seed=args.seed)
     else:
         q, k, v = workload_inputs(w, seed=args.seed)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o = torch.empty_like(qd)
+    o = torch.empty(tuple(q.shape), dtype=torch.float16, device=dev)
+    peak = PEAK_FP8_TFLOPS if w.path == "fp8" else PEAK_FP16_TFLOPS
     lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -233,6 +248,12 @@ def main() -> int:
         def step():
             fa.forward_splitkv(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse,
                                past_len=w.past_len, n_splits=n_splits, workspace=ws)
+    elif w.path == "fp8":
+        n_splits = None
+
+        def step():
+            fa.forward_fp8(qd, kd, vd, descale=descale, causal=w.causal, scale=w.scale, out=o,
+                           lse=lse, past_len=w.past_len)
     else:
         n_splits = None
 
@@ -273,9 +294,8 @@ def main() -> int:
                     "algorithmic_bytes": w.algorithmic_bytes}
     else:
         achieved = w.step_flops / (kernel_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                    "traffic": traffic}
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
         if w.path == "backward":
             roofline["flops_counted"] = "2.5 x 4*B*H*L^2*D (S, dP, dV, dK, dQ), causal halved"
     result = {
@@ -289,32 +309,35 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "e4m3" if w.path == "fp8" else "f16",
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "L": w.L, "D": w.D,
                    "causal": w.causal, "layout": "BSHD", "seed": args.seed,
                    **({"Lk": w.keys, "past_len": w.past_len} if w.keys != w.L else {}),
                    **({"entry_point": "fa_fwd_splitkv", "n_splits": n_splits}
                       if n_splits is not None else {}),
-                   **({"entry_point": "fa_bwd"} if w.path == "backward" else {})},
-        "pct_peak": round(100.0 * value / PEAK_FP16_TFLOPS, 2),
+                   **({"entry_point": "fa_bwd"} if w.path == "backward" else {}),
+                   **({"entry_point": "fa_fwd_fp8", "inputs": "E4M3, one descale per tensor",
+                       "output": "fp16"} if w.path == "fp8" else {})},
+        "pct_peak": round(100.0 * value / peak, 2),
         "roofline": roofline,
         "kernel_ms_mean": round(kernel_ms, 5),
         "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
         "kernel_sha": kernel_sha(),
     }
     print(f"[bench] {name}: {ms_per_step:.4f} ms/step, kernel {kernel_ms:.4f} ms, "
-          f"{value:.1f} TFLOP/s ({result['pct_peak']}% of {PEAK_FP16_TFLOPS})",
+          f"{value:.1f} TFLOP/s ({result['pct_peak']}% of {peak})",
           file=sys.stderr, flush=True)
     clock = sample_clock_power(step)
     if clock and (clock["gfxclk_mhz"] or 0) >= 500 and w.path != "splitkv":
         # the published peak assumes 2.4 GHz; the same peak at the clock the part ran
-        peak_at_clock = PEAK_FP16_TFLOPS * clock["gfxclk_mhz"] / 2400.0
+        peak_at_clock = peak * clock["gfxclk_mhz"] / 2400.0
         clock["peak_at_clock_tflops"] = round(peak_at_clock, 1)
         clock["frac_at_clock"] = round(achieved / peak_at_clock, 4)
     result["clock"] = clock
     if not args.no_cpu_baseline and w.path != "backward":
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds,
+                                              descale if w.path == "fp8" else None)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -1,6 +1,7 @@
 /*
- * fa.h -- C ABI of libfa.so, the attention forward pass for AMD Instinct
- * MI355X (gfx950).
+ * fa.h -- C ABI of libfa.so, the attention forward pass (fp16 and fp8
+ * inputs, split-KV decoding) and its backward pass for AMD Instinct MI355X
+ * (gfx950).
  *
  * Operation (page "使用 TileLang 在 AMD GPU 上快速开发高性能 Flash Attention",
  * sections "核心公式与计算流程" and "K/V Tile 遍历与核心计算"):
@@ -115,6 +116,42 @@ FA_API int fa_fwd_kv(const void *q, const void *k, const void *v, void *o, float
               float scale, hipStream_t stream);
 
 /*
+ * fa_fwd_fp8 -- the operation of fa_fwd_kv on 8-bit floating-point inputs
+ * (page "TileLang性能分析报告：H100上FlashAttention吞吐量达1.2PFlops", section
+ * "生产环境部署建议", names FP8 mixed precision as the next step for
+ * throughput).  q, k and v hold OCP FP8 E4M3 codes ("e4m3fn": 1 sign bit,
+ * 4 exponent bits with bias 7, 3 fraction bits, no infinities, S.1111.111 is
+ * NaN, largest finite 448), one descale factor per tensor: the value of a
+ * code c of q is q_descale * e4m3(c), likewise for k and v.  The scores are
+ * s_j = scale * q_descale * k_descale * sum_d q[i,d] * k[j,d] (exact E4M3
+ * products, fp32 accumulation), and
+ *   O   = v_descale * sum_j softmax_j(s) * v[j,:],   LSE = ln sum_j exp(s_j).
+ *
+ * The probabilities enter the second product as E4M3 (each stored as 8 times
+ * its weight relative to the row's running maximum: relative rounding error
+ * at most 2^-4 for weights down to 2^-9 of the maximum's); the row sums and
+ * the LSE use the unrounded fp32 probabilities.  O is fp16 (round to nearest
+ * even), LSE fp32, as for fa_fwd_kv.
+ *
+ * q       device pointer, E4M3 bytes, contiguous [B][Lq][H][D]      (read)
+ * k, v    device pointers, E4M3 bytes, contiguous [B][Lk][Hkv][D]   (read)
+ *         (NULL allowed when Lk == 0)
+ * o       device pointer, fp16, contiguous [B][Lq][H][D]            (written)
+ * lse     device pointer, fp32, contiguous [B][H][Lq], or NULL      (written)
+ * B .. scale, stream       as for fa_fwd_kv.
+ * q_descale, k_descale, v_descale   finite and > 0 (and scale * q_descale *
+ *         k_descale finite and > 0), else FA_ERR_SCALE.
+ *
+ * Ownership, alignment (16 bytes for q, k, v, o; 4 for lse), aliasing and
+ * the other errors as for fa_fwd_kv; the byte ranges of q, k, v are one byte
+ * per element.  B == 0 or Lq == 0 returns FA_OK and launches nothing.
+ */
+FA_API int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int B, int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len,
+                      float scale, float q_descale, float k_descale, float v_descale,
+                      hipStream_t stream);
+
+/*
  * fa_fwd_splitkv -- the same operation as fa_fwd_kv, computed by splitting
  * the key sequence (flash decoding; page "TileLang性能分析报告：H100上
  * FlashAttention吞吐量达1.2PFlops", section "生产环境部署建议", which names it
@@ -154,9 +191,12 @@ FA_API int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, 
                           float scale, int n_splits, void *workspace, long long workspace_bytes,
                           hipStream_t stream);
 
-/* The number of key splits fa_fwd_splitkv uses when passed n_splits = 0:
- * about 1024 work items over the GPU, no split shorter than 128 keys, at
- * least 1.  Pure host arithmetic; never fails. */
+/* The number of key splits fa_fwd_splitkv uses when passed n_splits = 0.
+ * Work items (one wavefront per row block and split) run in rounds of as
+ * many as the GPU holds at once (256 compute units x 160 KiB of LDS over
+ * 384*D bytes per wavefront); the choice minimises rounds x (32-key blocks
+ * per split + 2) over 1..64 splits, no split shorter than four blocks, ties
+ * to fewer splits.  At least 1.  Pure host arithmetic; never fails. */
 FA_API int fa_splitkv_splits(int B, int Lq, int Lk, int H, int Hkv, int D, int causal,
                              int past_len);
 
@@ -205,7 +245,8 @@ FA_API const char *fa_status_string(int status);
 
 /* Version of this ABI (bumped when an entry point is added or a signature or
  * a layout changes): 2 = fa_fwd, fa_fwd_kv; 3 adds fa_fwd_splitkv,
- * fa_splitkv_splits and fa_splitkv_workspace_bytes; 4 adds fa_bwd. */
+ * fa_splitkv_splits and fa_splitkv_workspace_bytes; 4 adds fa_bwd; 5 adds
+ * fa_fwd_fp8. */
 FA_API int fa_abi_version(void);
 
 #ifdef __cplusplus

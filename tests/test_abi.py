@@ -35,9 +35,9 @@ def declared_symbols():
 def test_library_loads_and_exports_header_symbols():
     lib = fa.library()
     names = declared_symbols()
-    assert set(names) == {"fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv", "fa_splitkv_splits",
-                          "fa_splitkv_workspace_bytes", "fa_bwd", "fa_status_string",
-                          "fa_abi_version"}
+    assert set(names) == {"fa_fwd", "fa_fwd_kv", "fa_fwd_fp8", "fa_fwd_splitkv",
+                          "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_bwd",
+                          "fa_status_string", "fa_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], check=True,
                          stdout=subprocess.PIPE, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -46,7 +46,7 @@ def test_library_loads_and_exports_header_symbols():
         assert hasattr(lib, n)
     # nothing beyond the declared C ABI leaks out of the library
     assert exported == set(names)
-    assert lib.fa_abi_version() == 4
+    assert lib.fa_abi_version() == 5
 
 
 def test_status_strings():
@@ -303,3 +303,40 @@ def test_bwd_empty_problems_are_noops():
     assert call_bwd(B=0, **nulls) == 0
     assert call_bwd(L=0, **nulls) == 0
     assert call_bwd(L=0, D=96) == 4
+
+
+# ------------------------------------------------------------ fp8 forward ABI
+
+FP8_ARGS = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=1, Lq=128, Lk=128, H=2, Hkv=2, D=64, causal=0,
+                past_len=0, scale=0.125, qd=0.01, kd=0.02, vd=0.03, stream=None)
+Q8_BYTES = 128 * 2 * 64  # one byte per element
+
+
+def call_fp8(**kw):
+    a = dict(FP8_ARGS)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"], a["Lk"], a["H"],
+                         a["Hkv"], a["D"], a["causal"], a["past_len"], a["scale"], a["qd"], a["kd"],
+                         a["vd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=-1), 2), (dict(Lk=(1 << 30) + 1), 2), (dict(past_len=-(1 << 30) - 1), 2),
+    (dict(H=3, Hkv=2), 3), (dict(D=96), 4),
+    (dict(scale=0.0), 5), (dict(qd=0.0), 5), (dict(kd=-1.0), 5), (dict(vd=math.nan), 5),
+    (dict(qd=math.inf), 5), (dict(scale=1e30, qd=1e30, kd=1e30), 5),
+    (dict(q=Q + 8), 6), (dict(k=K + 4), 6), (dict(o=O + 2), 6), (dict(lse=LSE + 1), 6),
+    # q, k, v span one byte per element, o two
+    (dict(o=Q + Q8_BYTES - 16), 7), (dict(o=K - 2 * Q8_BYTES + 16), 7), (dict(lse=V + 16), 7),
+    (dict(lse=O + 2 * Q8_BYTES - 16), 7),
+])
+def test_fp8_invalid_arguments_rejected_without_launch(kw, status):
+    assert call_fp8(**kw) == status
+
+
+def test_fp8_empty_problems_are_noops():
+    assert call_fp8(B=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert call_fp8(Lq=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert call_fp8(B=0, qd=0.0) == 5  # still validated
+    assert call_fp8(Lq=0, D=96) == 4

@@ -1,0 +1,201 @@
+"""GPU parity of the fp8 forward (fa_fwd_fp8) against the fp64 oracle.
+
+The oracle computes attention exactly on the decoded E4M3 values (times the
+descales).  The kernel differs from it in two ways, and the bar is built from
+both:
+
+1. It rounds the probabilities to E4M3 before the P.V product, each stored as
+   8 times its weight relative to the row's running maximum.  The oracle
+   returns the bound of that rounding per output element (model: relative
+   error 2^-4 for weights >= 2^-9 of the maximum's, at most min(w, 2^-13)
+   below; see fa_oracle.c and the oracle's own pins).
+2. The matrix unit sums the 64 E4M3 products of each instruction with less
+   than fp32 precision: within 2^-13 of the sum of the products' magnitudes
+   for E4M3 codes of Gaussian data (tests/test_mfma_layout.py checks this).
+   A row's scores are therefore off by at most
+       delta = 2^-13 * scale * q_descale * k_descale * max_j sum_d |q_d k_jd|,
+   which moves the LSE by at most delta and each probability by a factor
+   within e^{+-delta}; the output then moves by at most
+   (e^{2 delta} - e^{delta}) * (A_d + |O_d|) with A_d = sum_j P_j |V_jd|
+   (the oracle's bound function with the model (1, 0, 0)).
+
+Per element of O:
+    |O_gpu - O_ref| <= 1.02 e^{2 delta} bound + (e^{2 delta} - e^{delta}) (A + |O_ref|)
+                       + 2^-10 |O_ref| + 1e-5 max|V|
+(the last two: fp16 rounding of the output, fp32 accumulation and exp2), and
+per row of LSE (which uses the unrounded fp32 probabilities):
+    |LSE_gpu - LSE_ref| <= 1e-3 + delta.
+Rows that see no key must be exactly O = 0 and LSE = -inf.
+
+Cases: ragged lengths around the 32-row blocks and 64-key tiles, both head
+dims, causal and not; every grouped-query ratio; wide logits (Q, K x3, which
+drive the probabilities deep into E4M3's subnormal range and exercise the
+overrun fixup); queries after cached keys (past_len, also negative); no keys;
+descales far from 1; the two fp8 workloads at full size on sampled rows; and
+properties: determinism, LSE optional, argument errors.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_attention_flash_amd as fa
+from tiled_attention_flash_amd.inputs import WORKLOADS, make_qkv_fp8
+
+pytestmark = pytest.mark.gpu
+
+MODEL = (2.0 ** -4, 2.0 ** -9, 2.0 ** -13)
+ABS_MODEL = (1.0, 0.0, 0.0)  # bound function -> sum_j P_j |V_jd|
+MAX_LSE = 1e-3
+U_MFMA8 = 2.0 ** -13  # sum error of the E4M3 matrix unit, relative to sum |products|
+
+
+def run_gpu(q8, k8, v8, ds, causal, scale=None, past_len=None):
+    o, lse = fa.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), descale=ds, causal=causal, scale=scale,
+                            past_len=past_len)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def vmax(v8, vd):
+    return float(v8.view(torch.float8_e4m3fn).float().abs().max()) * vd if v8.numel() else 0.0
+
+
+def score_slack(q8, k8, ds, scale, rows=None):
+    """delta per row (b, h, i): U_MFMA8 * scale * qd * kd * max_j sum_d |q_d k_jd|
+    over all keys (a superset of the visible ones).  rows: [n, 3] or None for
+    every row ([B, H, Lq])."""
+    Q = np.abs(q8.view(torch.float8_e4m3fn).double().numpy())  # [B, Lq, H, D]
+    K = np.abs(k8.view(torch.float8_e4m3fn).double().numpy())  # [B, Lk, Hkv, D]
+    B, Lq, H, D = Q.shape
+    Hkv = K.shape[2]
+    g = H // Hkv
+    c = U_MFMA8 * scale * ds[0] * ds[1]
+    if K.shape[1] == 0:
+        return np.zeros((B, H, Lq)) if rows is None else np.zeros(len(rows))
+    if rows is None:
+        out = np.zeros((B, H, Lq))
+        for b in range(B):
+            for h in range(H):
+                out[b, h] = (Q[b, :, h] @ K[b, :, h // g].T).max(axis=1)
+        return c * out
+    return c * np.array([(K[b, :, h // g] @ Q[b, i, h]).max() for b, h, i in rows])
+
+
+def check_rows(o, lse, ro, rl, bound, absv, delta, vmx, where=""):
+    """o, ro, bound, absv: [n, D] rows; lse, rl, delta: [n]."""
+    seen = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse), seen), f"{where}: rows with no key differ"
+    assert np.all(lse[~seen] == -np.inf), where
+    assert np.all(o[~seen] == 0.0), where
+    if not seen.any():
+        return 0.0
+    dl = np.abs(lse[seen] - rl[seen])
+    worst_l = np.max(dl / (MAX_LSE + delta[seen]))
+    assert worst_l <= 1.0, f"{where}: |dLSE| {worst_l:.3f} x its bar (max {dl.max():.3e})"
+    e1, e2 = np.exp(delta[seen])[:, None], np.exp(2 * delta[seen])[:, None]
+    err = np.abs(o[seen] - ro[seen])
+    lim = (1.02 * e2 * bound[seen] + (e2 - e1) * (absv[seen] + np.abs(ro[seen]))
+           + 2.0 ** -10 * np.abs(ro[seen]) + 1e-5 * vmx)
+    worst = np.max(err / lim)
+    assert worst <= 1.0, f"{where}: error {worst:.3f} x its bar"
+    return float(worst)
+
+
+def full_case(B, Lq, Lk, H, Hkv, D, causal, seed, mult=1.0, past_len=None, ds_mult=(1, 1, 1)):
+    q8, k8, v8, ds = make_qkv_fp8(B, Lq, H, Hkv, D, seed=seed, qk_mult=mult, Lk=Lk)
+    ds = tuple(d * m for d, m in zip(ds, ds_mult))
+    past = Lk - Lq if past_len is None else past_len
+    scale = 1.0 / np.sqrt(D)
+    o, lse = run_gpu(q8, k8, v8, ds, causal, scale=scale, past_len=past)
+    ro, rl, bound = oracle.forward_fp8(q8, k8, v8, ds, causal=causal, scale=scale, past_len=past,
+                                       bound_model=MODEL)
+    _, _, absv = oracle.forward_fp8(q8, k8, v8, ds, causal=causal, scale=scale, past_len=past,
+                                    bound_model=ABS_MODEL)
+    delta = score_slack(q8, k8, ds, scale)
+    # [B, Lq, H, D] and [B, H, Lq] -> rows (b, h, i)
+    rows = lambda x: np.transpose(x, (0, 2, 1, 3)).reshape(-1, D)
+    return check_rows(rows(o), lse.reshape(-1), rows(ro), rl.reshape(-1), rows(bound), rows(absv),
+                      delta.reshape(-1), vmax(v8, ds[2]),
+                      f"B={B} Lq={Lq} Lk={Lk} H={H} Hkv={Hkv} D={D} causal={causal} past={past}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("L", [1, 3, 63, 64, 65, 127, 129, 200, 257, 511])
+def test_fp8_ragged_lengths(L, causal, D):
+    full_case(1, L, L, 2, 2, D, causal, seed=L)
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+def test_fp8_gqa(g):
+    full_case(2, 300, 300, 8, 8 // g, 128, True, seed=40 + g)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_wide_logits(D, causal):
+    full_case(1, 384, 384, 4, 2, D, causal, seed=7, mult=3.0)
+
+
+@pytest.mark.parametrize("Lq,Lk,past", [(1, 300, None), (77, 500, None), (200, 130, None),
+                                          (100, 100, 37), (90, 120, -20), (64, 64, 300)])
+def test_fp8_queries_after_cached_keys(Lq, Lk, past):
+    for causal in (False, True):
+        full_case(1, Lq, Lk, 4, 2, 128, causal, seed=Lq + Lk, past_len=past)
+
+
+def test_fp8_no_keys():
+    q8, _, _, ds = make_qkv_fp8(1, 40, 2, 2, 64, seed=3)
+    empty = torch.empty((1, 0, 2, 64), dtype=torch.uint8)
+    o, lse = run_gpu(q8, empty, empty, ds, False)
+    assert np.all(o == 0.0) and np.all(lse == -np.inf)
+
+
+def test_fp8_descales_far_from_one():
+    full_case(1, 150, 150, 2, 1, 128, True, seed=9, ds_mult=(64.0, 1.0 / 32, 1000.0))
+
+
+@pytest.mark.parametrize("name", ["fp8-mha-b8-h32-L4096-d128", "fp8-mha-b8-h32-L4096-d128-causal"])
+def test_fp8_workloads_sampled_rows(name):
+    w = WORKLOADS[name]
+    q8, k8, v8, ds = make_qkv_fp8(w.B, w.L, w.H, w.Hkv, w.D, seed=0)
+    o, lse = fa.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), descale=ds, causal=w.causal)
+    torch.cuda.synchronize()
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    rng = np.random.default_rng(5)
+    edges = [0, 1, 31, 32, 63, 64, 255, 256, 2047, 2048, w.L - 1]
+    rows = [(b, h, i) for b, h, i in zip(rng.integers(0, w.B, 48), rng.integers(0, w.H, 48),
+                                          rng.integers(0, w.L, 48))]
+    rows += [(int(rng.integers(0, w.B)), int(rng.integers(0, w.H)), i) for i in edges]
+    rows += [(w.B - 1, h, w.L - 1 - h) for h in range(w.H)]
+    rows = np.array(rows, np.int64)
+    ro, rl, bound = oracle.rows_fp8(q8, k8, v8, rows, ds, causal=w.causal, bound_model=MODEL)
+    _, _, absv = oracle.rows_fp8(q8, k8, v8, rows, ds, causal=w.causal, bound_model=ABS_MODEL)
+    go = o[rows[:, 0], rows[:, 2], rows[:, 1]]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    delta = score_slack(q8, k8, ds, w.scale, rows)
+    check_rows(go, gl, ro, rl, bound, absv, delta, vmax(v8, ds[2]), name)
+    assert np.all(np.isfinite(o))
+
+
+def test_fp8_deterministic_and_lse_optional():
+    q8, k8, v8, ds = make_qkv_fp8(2, 700, 8, 2, 128, seed=12)
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+    o1, l1 = fa.forward_fp8(q8, k8, v8, descale=ds, causal=True)
+    o2, l2 = fa.forward_fp8(q8, k8, v8, descale=ds, causal=True)
+    o3, l3 = fa.forward_fp8(q8, k8, v8, descale=ds, causal=True, with_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3) and l3 is None
+
+
+def test_fp8_argument_errors():
+    q8, k8, v8, ds = make_qkv_fp8(1, 64, 2, 2, 64, seed=1)
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+    with pytest.raises(fa.FaError) as e:
+        fa.forward_fp8(q8, k8, v8, descale=(0.0, 1.0, 1.0))
+    assert e.value.status == 5
+    with pytest.raises(TypeError):
+        fa.forward_fp8(q8.half(), k8, v8)

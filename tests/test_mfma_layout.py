@@ -69,3 +69,167 @@ def test_fp16_pack_rounds_to_nearest_even(probe):
     torch.cuda.synchronize()
     want = x.astype(np.float16)  # numpy rounds to nearest even
     assert np.array_equal(y.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+# ---------------------------------------------------------------- fp8 forms
+#
+# The fp8 kernel assumes, for v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands
+# (D = A[32x64] . B[64x32], 32 bytes per lane):
+#   lane l holds A[l % 32][32 * (l // 32) + i] and B[32 * (l // 32) + i][l % 32]
+#   in byte i = 0..31, the result as for the fp16 form, every code decoded
+#   as OCP E4M3 (torch's float8_e4m3fn), the scaled form with unit scales
+#   equal to the plain one;
+# for ds_read_b64_tr_b8: lane j of each 16-lane group receives, as byte b,
+#   byte j % 8 of the 8 bytes that lane 2b + j // 8 of the group points at;
+# for the fp32 -> E4M3 pair conversion: torch's rounding (nearest even,
+#   448 at the top), bytes in argument order, low then high half;
+# and a bound on the error of the unit's 64-term sums.
+
+def _e4m3(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).double().numpy()
+
+
+@pytest.mark.parametrize("scaled", [0, 1])
+def test_mfma_32x32x64_fp8_layout(probe, scaled):
+    rng = np.random.default_rng(2 + scaled)
+    # codes on a 0.25 grid (0, +-0.25 .. +-3): products and 64-term sums are
+    # exact in fp32 (with wider ranges the unit rounds its sums)
+    pool = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0xB0, 0xB8, 0xC0, 0x28, 0xBC, 0xC4],
+                    np.uint8)
+    A = pool[rng.integers(0, len(pool), (32, 64))]
+    B = pool[rng.integers(0, len(pool), (64, 32))]
+    a_lanes = np.zeros((64, 32), np.uint8)
+    b_lanes = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        for i in range(32):
+            a_lanes[l, i] = A[l % 32, 32 * (l // 32) + i]
+            b_lanes[l, i] = B[32 * (l // 32) + i, l % 32]
+    a = torch.from_numpy(a_lanes).cuda()
+    b = torch.from_numpy(b_lanes).cuda()
+    c = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert probe.probe_mfma_32x32x64_f8(a.data_ptr(), b.data_ptr(), c.data_ptr(), scaled, s) == 0
+    torch.cuda.synchronize()
+    got = c.cpu().numpy()
+    want = _e4m3(A) @ _e4m3(B)
+    for l in range(64):
+        for I in range(4):
+            for J in range(4):
+                assert got[l, 4 * I + J] == want[8 * I + 4 * (l // 32) + J, l % 32], (l, I, J)
+
+
+def test_mfma_fp8_decodes_every_code(probe):
+    """Row m of A holds 64 codes, B picks one k per output column: every
+    non-NaN code appears and comes out as its E4M3 value."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)  # 254 codes
+    s = torch.cuda.current_stream().cuda_stream
+    for start in range(0, len(codes), 64 * 4):
+        chunk = codes[start:start + 64 * 4]
+        A = np.zeros((32, 64), np.uint8)
+        A[: (len(chunk) + 63) // 64].flat[: len(chunk)] = chunk
+        for half in range(2):  # column n picks k = 32 * half + n
+            Bh = np.zeros((64, 32), np.uint8)
+            for n in range(32):
+                Bh[32 * half + n, n] = 0x38
+            a_lanes = np.zeros((64, 32), np.uint8)
+            b_lanes = np.zeros((64, 32), np.uint8)
+            for l in range(64):
+                for i in range(32):
+                    a_lanes[l, i] = A[l % 32, 32 * (l // 32) + i]
+                    b_lanes[l, i] = Bh[32 * (l // 32) + i, l % 32]
+            c = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+            a, b = torch.from_numpy(a_lanes).cuda(), torch.from_numpy(b_lanes).cuda()
+            assert probe.probe_mfma_32x32x64_f8(a.data_ptr(), b.data_ptr(), c.data_ptr(), 0, s) == 0
+            torch.cuda.synchronize()
+            got = c.cpu().numpy()
+            for l in range(64):
+                for I in range(4):
+                    for J in range(4):
+                        m, n = 8 * I + 4 * (l // 32) + J, l % 32
+                        assert got[l, 4 * I + J] == _e4m3(A[m, 32 * half + n:32 * half + n + 1])[0]
+
+
+@pytest.mark.parametrize("amax", [448.0, 4.0])
+def test_mfma_fp8_sum_error_model(probe, amax):
+    """The E4M3 matrix unit sums each output's 64 products with less than fp32
+    precision.  The fp8 parity bar assumes, for E4M3 codes of Gaussian data
+    (each matrix scaled to the given largest magnitude, then rounded by
+    torch's E4M3 cast), |error| <= 2^-13 * sum_k |A_mk B_kn| (measured worst
+    case about 2^-15; random codes over the whole E4M3 range reach 2^-11.7
+    and are not covered)."""
+    rng = np.random.default_rng(int(amax))
+    s = torch.cuda.current_stream().cuda_stream
+    worst = 0.0
+    for _ in range(24):
+        x = rng.normal(size=(32, 64))
+        y = rng.normal(size=(64, 32))
+        A = torch.from_numpy(x * amax / np.abs(x).max()).float().to(torch.float8_e4m3fn).view(
+            torch.uint8).numpy()
+        B = torch.from_numpy(y * amax / np.abs(y).max()).float().to(torch.float8_e4m3fn).view(
+            torch.uint8).numpy()
+        a_lanes = np.zeros((64, 32), np.uint8)
+        b_lanes = np.zeros((64, 32), np.uint8)
+        for l in range(64):
+            a_lanes[l] = A[l % 32, 32 * (l // 32):32 * (l // 32) + 32]
+            b_lanes[l] = B[32 * (l // 32):32 * (l // 32) + 32, l % 32]
+        a, b = torch.from_numpy(a_lanes).cuda(), torch.from_numpy(b_lanes).cuda()
+        c = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+        assert probe.probe_mfma_32x32x64_f8(a.data_ptr(), b.data_ptr(), c.data_ptr(), 0, s) == 0
+        torch.cuda.synchronize()
+        got = c.cpu().numpy().astype(np.float64)
+        Ad, Bd = _e4m3(A), _e4m3(B)
+        exact, mag = Ad @ Bd, np.abs(Ad) @ np.abs(Bd)
+        for l in range(64):
+            for I in range(4):
+                for J in range(4):
+                    m, n = 8 * I + 4 * (l // 32) + J, l % 32
+                    worst = max(worst, abs(got[l, 4 * I + J] - exact[m, n]) / mag[m, n])
+    assert worst <= 2.0 ** -13, worst
+
+
+@pytest.mark.parametrize("pattern", ["linear", "permuted", "rows"])
+def test_ds_read_tr8_lane_mapping(probe, pattern):
+    idx = np.arange(1024)
+    if pattern == "linear":
+        addr = 8 * np.arange(64)
+    elif pattern == "permuted":
+        addr = 8 * (np.arange(64) ^ 5)
+    else:
+        addr = np.array([(l % 16) * 64 + (l // 16) * 8 for l in range(64)])
+    addr = addr.astype(np.int32)
+    assert addr.min() >= 0 and addr.max() <= 1016 and not (addr & 7).any()
+    import ctypes
+    s = torch.cuda.current_stream().cuda_stream
+    got = {}
+    for part, src in (("lo", idx & 255), ("hi", idx >> 8)):
+        sb = torch.from_numpy(src.astype(np.uint8)).cuda()
+        ad = torch.from_numpy(addr).cuda()
+        o = torch.zeros(64 * 8, dtype=torch.uint8, device="cuda")
+        ah = (ctypes.c_int * 64)(*addr.tolist())
+        assert probe.probe_ds_read_tr8(sb.data_ptr(), ah, ad.data_ptr(), o.data_ptr(), s) == 0
+        torch.cuda.synchronize()
+        got[part] = o.cpu().numpy().reshape(64, 8).astype(int)
+    src_addr = got["lo"] + 256 * got["hi"]
+    for l in range(64):
+        g, j = l // 16, l % 16
+        for b in range(8):
+            assert src_addr[l, b] == addr[16 * g + 2 * b + j // 8] + j % 8, (l, b)
+
+
+def test_fp8_pack_matches_torch_rounding(probe):
+    vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    fin = np.sort(np.unique(vals[np.isfinite(vals)]))
+    mids = (fin[1:] + fin[:-1]) / 2
+    rng = np.random.default_rng(4)
+    x = np.concatenate([fin, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+                        rng.normal(size=1000) * 50, [448.0, 455.0, 2.0 ** -10, 3 * 2.0 ** -11,
+                                                     2.0 ** -12, 1e-30]]).astype(np.float32)
+    x = np.concatenate([x, np.zeros((-len(x)) % 4, np.float32)])
+    xd = torch.from_numpy(x).cuda()
+    y = torch.zeros(len(x), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert probe.probe_cvt_fp8(xd.data_ptr(), y.data_ptr(), len(x), s) == 0
+    torch.cuda.synchronize()
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(y.cpu().numpy(), want)

@@ -18,6 +18,14 @@ Lk - Lq, which the causal mask uses.
 computes the same result by splitting the keys over separate wavefronts and
 merging the partial results (for few query rows against many keys); its fp32
 workspace is allocated with torch unless one is passed.
+
+    o, lse = tiled_attention_flash_amd.forward_fp8(q8, k8, v8, descale=(qd, kd, vd))
+
+takes E4M3 inputs (one descale per tensor) and returns fp16 o, fp32 lse;
+
+    dq, dk, dv, delta = tiled_attention_flash_amd.backward(q, k, v, o, lse, dout)
+
+computes the gradients of sum(o * dout).
 """
 from __future__ import annotations
 
@@ -25,7 +33,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "forward_splitkv", "backward", "fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv", "fa_bwd",
+__all__ = ["forward", "forward_splitkv", "forward_fp8", "backward", "fa_fwd", "fa_fwd_kv",
+           "fa_fwd_splitkv", "fa_fwd_fp8", "fa_bwd",
            "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_status_string", "library",
            "library_path", "FaError", "STATUS"]
 
@@ -71,6 +80,8 @@ def library():
     lib.fa_splitkv_splits.restype = c_int
     lib.fa_splitkv_workspace_bytes.argtypes = [c_int] * 5
     lib.fa_splitkv_workspace_bytes.restype = ctypes.c_longlong
+    lib.fa_fwd_fp8.argtypes = ([vp, vp, vp, vp, vp] + [c_int] * 8 + [ctypes.c_float] * 4 + [vp])
+    lib.fa_fwd_fp8.restype = c_int
     lib.fa_bwd.argtypes = [vp] * 10 + [c_int] * 6 + [ctypes.c_float, vp]
     lib.fa_bwd.restype = c_int
     lib.fa_status_string.argtypes = [c_int]
@@ -115,6 +126,51 @@ def fa_splitkv_splits(B, Lq, Lk, H, Hkv, D, causal, past_len) -> int:
 def fa_splitkv_workspace_bytes(B, Lq, H, D, n_splits) -> int:
     return int(library().fa_splitkv_workspace_bytes(int(B), int(Lq), int(H), int(D),
                                                     int(n_splits)))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, q_descale,
+               k_descale, v_descale, stream) -> int:
+    return int(library().fa_fwd_fp8(q, k, v, o, lse, int(B), int(Lq), int(Lk), int(H), int(Hkv),
+                                    int(D), int(bool(causal)), int(past_len), float(scale),
+                                    float(q_descale), float(k_descale), float(v_descale), stream))
+
+
+def forward_fp8(q, k, v, descale=(1.0, 1.0, 1.0), causal: bool = False,
+                scale: float | None = None, out=None, lse=None, with_lse: bool = True,
+                past_len: int | None = None):
+    """Attention forward on E4M3 inputs (uint8 or float8_e4m3fn tensors, BSHD,
+    contiguous) with per-tensor descales (q, k, v) on the current stream.
+    Returns (o, lse): o float16 shaped like q, lse float32 [B, H, Lq] (None
+    when ``with_lse`` is False and no buffer is given)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if (not isinstance(t, torch.Tensor) or t.dtype not in (torch.uint8, torch.float8_e4m3fn)
+                or not t.is_cuda):
+            raise TypeError(f"{name} must be a uint8 / float8_e4m3fn tensor on a HIP device")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D [B, L, heads, D] tensor")
+    B, L, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, L, H, D), dtype=torch.float16, device=q.device)
+    out, lse = _outputs(out, out, lse, with_lse)
+    past = Lk - L if past_len is None else int(past_len)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd_fp8(q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
+                        out.data_ptr() or None,
+                        (lse.data_ptr() or None) if lse is not None else None, B, L, Lk, H, Hkv,
+                        D, causal, past, scale, descale[0], descale[1], descale[2], stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out, lse
 
 
 def _check_qkv(q, k, v):

@@ -20,7 +20,8 @@ ARCH = "gfx950"
 # Packed-fp32 VALU forms are switched off for every HIP translation unit.
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["fa_host.cpp", "fa_fwd_kernel.hip", "fa_splitkv_kernel.hip", "fa_bwd_kernel.hip"]
+SOURCES = ["fa_host.cpp", "fa_fwd_kernel.hip", "fa_fwd_fp8_kernel.hip", "fa_splitkv_kernel.hip",
+           "fa_bwd_kernel.hip"]
 
 
 def hipcc() -> str:

@@ -28,11 +28,13 @@ bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
 
 bool misaligned(const void *p, uintptr_t to) { return ((uintptr_t)p & (to - 1)) != 0; }
 
-// Shared argument validation of every entry point.  Returns FA_OK with *p
-// filled in, FA_OK with *empty set when there is nothing to compute, or an
-// error status.
+// Shared argument validation of every forward entry point.  in_size is the
+// byte size of a q/k/v element (2 for fp16, 1 for E4M3); o is always fp16.
+// Returns FA_OK with *p filled in, FA_OK with *empty set when there is
+// nothing to compute, or an error status.
 int validate(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Lq, int Lk,
-             int H, int Hkv, int D, int causal, int past_len, float scale, fa::Problem *p, bool *empty)
+             int H, int Hkv, int D, int causal, int past_len, float scale, fa::Problem *p, bool *empty,
+             int in_size = 2)
 {
     *empty = false;
     if (B < 0 || Lq < 0 || Lk < 0 || H < 0 || Hkv < 0 || D < 0) return FA_ERR_SHAPE;
@@ -59,9 +61,10 @@ int validate(const void *q, const void *k, const void *v, void *o, float *lse, i
         misaligned(lse, 4))
         return FA_ERR_ALIGN;
 
-    const int64_t q_bytes = q_elems * 2, kv_bytes = kv_elems * 2, lse_bytes = lse_elems * 4;
-    if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) ||
-        overlaps(o, q_bytes, v, kv_bytes) || overlaps(o, q_bytes, lse, lse_bytes) ||
+    const int64_t q_bytes = q_elems * in_size, kv_bytes = kv_elems * in_size;
+    const int64_t o_bytes = q_elems * 2, lse_bytes = lse_elems * 4;
+    if (overlaps(o, o_bytes, q, q_bytes) || overlaps(o, o_bytes, k, kv_bytes) ||
+        overlaps(o, o_bytes, v, kv_bytes) || overlaps(o, o_bytes, lse, lse_bytes) ||
         overlaps(lse, lse_bytes, q, q_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
         overlaps(lse, lse_bytes, v, kv_bytes))
         return FA_ERR_ALIAS;
@@ -136,6 +139,24 @@ extern "C" int fa_fwd_kv(const void *q, const void *k, const void *v, void *o, f
                          float scale, hipStream_t stream)
 {
     return forward(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, stream);
+}
+
+extern "C" int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                          int Lq, int Lk, int H, int Hkv, int D, int causal, int past_len,
+                          float scale, float q_descale, float k_descale, float v_descale,
+                          hipStream_t stream)
+{
+    fa::Problem p;
+    bool empty;
+    const int st =
+        validate(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, &p, &empty, 1);
+    if (st != FA_OK) return st;
+    for (float d : {q_descale, k_descale, v_descale})
+        if (!isfinite(d) || !(d > 0.0f)) return FA_ERR_SCALE;
+    if (!isfinite(scale * q_descale * k_descale) || !(scale * q_descale * k_descale > 0.0f))
+        return FA_ERR_SCALE;
+    if (empty) return FA_OK;
+    return fa::launch_forward_fp8(p, fa::Fp8Descale{q_descale, k_descale, v_descale}, stream);
 }
 
 extern "C" int fa_splitkv_splits(int B, int Lq, int Lk, int H, int Hkv, int D, int causal,
@@ -224,7 +245,7 @@ extern "C" const char *fa_status_string(int status)
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative size, size overflow, or |past_len| > 2^30";
     case FA_ERR_GQA: return "FA_ERR_GQA: H and Hkv must be positive and H a multiple of Hkv";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
-    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale (and fp8 descales) must be finite and > 0";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o need 16-byte, lse 4-byte alignment";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: o or lse overlaps another tensor";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
@@ -236,4 +257,4 @@ extern "C" const char *fa_status_string(int status)
     }
 }
 
-extern "C" int fa_abi_version(void) { return 4; }
+extern "C" int fa_abi_version(void) { return 5; }

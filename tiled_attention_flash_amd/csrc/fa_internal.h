@@ -1,5 +1,5 @@
 // fa_internal.h -- interface between the C-ABI front end (fa_host.cpp) and the
-// kernel translation unit (fa_fwd_kernel.hip).  Not installed, not part of
+// kernel translation units.  Not installed, not part of
 // the ABI.
 #pragma once
 
@@ -23,6 +23,14 @@ struct Problem {
 
 // Enqueues the forward kernels on `stream`.  Returns FA_OK or FA_ERR_LAUNCH.
 int launch_forward(const Problem &p, hipStream_t stream);
+
+// Forward on E4M3 inputs: q, k, v in p hold E4M3 codes, the value of a code
+// is its descale factor times its E4M3 value.  Returns FA_OK, FA_ERR_SHAPE
+// or FA_ERR_LAUNCH.
+struct Fp8Descale {
+    float q, k, v;
+};
+int launch_forward_fp8(const Problem &p, Fp8Descale ds, hipStream_t stream);
 
 // Split-KV forward: bytes of fp32 workspace for rows_total = B*H*Lq output
 // rows and n_splits key splits (-1 on overflow), and the launcher of the
