@@ -13,9 +13,11 @@
 // ------------------
 // * Workgroup = W wavefronts owning one block of BM = 32*W query rows of one
 //   (batch, query head); each wavefront owns 32 whole query rows.  W = 8 for
-//   the full (non-causal) pass -- each K/V tile brought into LDS then serves
-//   256 queries -- and W = 4 under the causal mask, where the smaller block
-//   keeps the wavefronts of a workgroup evenly loaded along the diagonal.
+//   the full (non-causal) pass at D = 128 -- each K/V tile brought into LDS
+//   then serves 256 queries -- and W = 4 under the causal mask, where the
+//   smaller block keeps the wavefronts of a workgroup evenly loaded along the
+//   diagonal, and at D = 64, where the shorter tiles favour two independent
+//   workgroups per CU (measured: 12% faster at L = 1024).
 // * Both products are computed transposed, on v_mfma_f32_32x32x16_f16:
 //     S^T[key][query]  = K . Q^T     (A = K rows from LDS, B = Q in VGPRs)
 //     O^T[d][query]   += V^T . P^T   (A = V^T from LDS,   B = P in VGPRs)
@@ -449,7 +451,7 @@ fa_fwd_kernel(const Args a)
 template <int D, bool CAUSAL>
 int launch(Args args, hipStream_t stream)
 {
-    constexpr int W = CAUSAL ? 4 : 8;
+    constexpr int W = (CAUSAL || D == 64) ? 4 : 8;
     using K = Kernel<D, CAUSAL, W>;
     args.n_qblocks = (args.Lq + K::kBM - 1) / K::kBM;
     const int64_t items = (int64_t)args.n_items * args.n_qblocks;  // n_items holds B*H here
