@@ -507,7 +507,9 @@ int launch_bwd(BwdArgs a, int B, hipStream_t stream)
     }
     // dK, dV
     {
-        constexpr int W = 4;
+        // eight wavefronts (256 keys per workgroup, one per CU) for the full
+        // pass at D = 128, four otherwise (measured per workload)
+        constexpr int W = (D == 128 && !CAUSAL) ? 8 : 4;
         BwdArgs b = a;
         b.n_blocks_item = (a.L + 32 * W - 1) / (32 * W);
         const int64_t items = (int64_t)B * a.Hkv * b.n_blocks_item;
@@ -518,7 +520,7 @@ int launch_bwd(BwdArgs a, int B, hipStream_t stream)
     }
     // dQ
     {
-        constexpr int W = CAUSAL ? 4 : 8;
+        constexpr int W = (CAUSAL || D == 64) ? 4 : 8;
         BwdArgs b = a;
         b.n_blocks_item = (a.L + 32 * W - 1) / (32 * W);
         const int64_t items = (int64_t)B * a.H * b.n_blocks_item;
