@@ -36,10 +36,11 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kSB = 32;               // keys per score block (one 32x32 accumulator)
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
-// A lane's sum of the fp16 probabilities of one score block at or above which
-// the block is recomputed against its own maximum.  Every kept probability
-// is then below 2^15, far from fp16's largest finite value (65504), and a
-// probability that overflowed to inf always fails the test.
+// A lane's sum of the (fp32) probabilities of one score block at or above
+// which the block is recomputed against its own maximum.  Every kept
+// probability is then below 2^15, far from fp16's largest finite value
+// (65504), and a probability that would round to inf in fp16, or is inf in
+// fp32, always fails the test.
 constexpr float kSumLimit = 32768.0f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -283,9 +284,11 @@ struct WaveMath {
 
     // P = exp2(S*c - m*c) for score pair p (registers 2p, 2p+1), rounded to
     // fp16 (round-to-nearest-even) into the B operand of k-step cs = p/4 of
-    // the P.V product at position 2(p%4).  The row sum adds exactly those
-    // fp16 values (the weights the P.V product applies), two per
-    // v_dot2_f32_f16, into two fp32 partial sums.
+    // the P.V product at position 2(p%4).  The row sum adds the fp32 values,
+    // one per partial sum: plain adds run beside the matrix unit, while a
+    // v_dot2_f32_f16 over the fp16 values waits for it (measured: about 11
+    // cycles each with MFMAs in flight).  The sum differs from that of the
+    // fp16 weights by at most one fp16 rounding (2^-11 relative).
     __device__ __forceinline__ static void exp_pair(const floatx16 &sc, half8 (&pf)[kCS], float (&rs)[2],
                                                     int p, float mc, float c)
     {
@@ -294,13 +297,13 @@ struct WaveMath {
         const float p1 = exp2_fast(__builtin_fmaf(sc[r + 1], c, -mc));
         const float2v f2 = {p0, p1};
         const half2v h2 = __builtin_convertvector(f2, half2v);
-        const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-        rs[p & 1] = __builtin_amdgcn_fdot2(h2, ones, rs[p & 1], false);
+        rs[0] += p0;
+        rs[1] += p1;
         pf[cs][e] = h2[0];
         pf[cs][e + 1] = h2[1];
         // keep the pair where it stands in the schedule: without a use here
         // the compiler sinks it towards its first MFMA
-        __asm__ volatile("" ::"v"(h2), "v"(rs[p & 1]));
+        __asm__ volatile("" ::"v"(h2), "v"(rs[0]), "v"(rs[1]));
     }
 };
 
