@@ -310,6 +310,9 @@ struct Kernel8 {
                                                 int qp, float c)
     {
         if constexpr (MASK) mask(sc, k0, Lk, qp);
+        // issue priority up for the exponential phase, down for P.V, so the
+        // other wavefront of the SIMD feeds the matrix unit meanwhile
+        __builtin_amdgcn_s_setprio(1);
         int8v pf;
         float rs[2] = {0.0f, 0.0f};
         const float mc = st.mc;
@@ -324,6 +327,7 @@ struct Kernel8 {
         int8v va = vfrag(st, vl, 0);
         if (__builtin_amdgcn_ballot_w64(rs[0] + rs[1] >= kE4M3Max)) fixup(st, sc, pf, rs, c);
         st.l += rs[0] + rs[1];
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int i = 0; i < kDBlocks; ++i) {
             int8v vn = va;
