@@ -238,3 +238,19 @@ def test_query_and_key_lengths_differ(case, causal):
                f"max|dO|={d.max():.3e} mean|dO|={d.mean():.3e} max|dLSE|={dl.max():.3e}")
         print(msg, flush=True)
         assert d.max() <= MAX_O and d.mean() <= MEAN_O and dl.max() <= MAX_LSE, msg
+
+
+# Under the causal mask, 8192 keys or more select the eight-wavefront (256-row)
+# forward instance; these cases cover its ragged ends, grouped heads and a
+# cached prefix, every row against the oracle.
+LONG_CAUSAL_CASES = [
+    (1, 8257, 8257, 2, 1, 128, None),   # ragged against 256-row blocks and 64-key tiles
+    (1, 300, 8300, 2, 2, 128, None),    # queries after 8000 cached keys
+    (1, 8192, 8192, 4, 1, 128, None),   # four query heads per K/V head
+]
+
+
+@pytest.mark.parametrize("case", LONG_CAUSAL_CASES,
+                         ids=[f"q{c[1]}-k{c[2]}-h{c[3]}-kv{c[4]}" for c in LONG_CAUSAL_CASES])
+def test_long_causal_ragged(case):
+    test_query_and_key_lengths_differ(case, True)

@@ -16,8 +16,9 @@
 //   the full (non-causal) pass at D = 128 -- each K/V tile brought into LDS
 //   then serves 256 queries -- and W = 4 under the causal mask, where the
 //   smaller block keeps the wavefronts of a workgroup evenly loaded along the
-//   diagonal, and at D = 64, where the shorter tiles favour two independent
-//   workgroups per CU (measured: 12% faster at L = 1024).
+//   diagonal (W = 8 again from 8192 keys on, where the diagonal is a small
+//   share of each work item), and at D = 64, where the shorter tiles favour
+//   two independent workgroups per CU.
 // * Both products are computed transposed, on v_mfma_f32_32x32x16_f16:
 //     S^T[key][query]  = K . Q^T     (A = K rows from LDS, B = Q in VGPRs)
 //     O^T[d][query]   += V^T . P^T   (A = V^T from LDS,   B = P in VGPRs)
@@ -459,10 +460,9 @@ fa_fwd_kernel(const Args a)
     Kernel<D, CAUSAL, W>::run(a);
 }
 
-template <int D, bool CAUSAL>
-int launch(Args args, hipStream_t stream)
+template <int D, bool CAUSAL, int W>
+int launch_w(Args args, hipStream_t stream)
 {
-    constexpr int W = (CAUSAL || D == 64) ? 4 : 8;
     using K = Kernel<D, CAUSAL, W>;
     args.n_qblocks = (args.Lq + K::kBM - 1) / K::kBM;
     const int64_t items = (int64_t)args.n_items * args.n_qblocks;  // n_items holds B*H here
@@ -471,6 +471,23 @@ int launch(Args args, hipStream_t stream)
     hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, W>), dim3(args.n_items), dim3(K::kThreads), 0,
                        stream, args);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Wavefronts per workgroup, measured per workload (same-process A/B): 8 for
+// the full pass at D = 128 (each K/V tile serves 256 queries); 4 at D = 64
+// and under the causal mask, where a 256-row block leaves half its
+// wavefronts computing masked blocks along the diagonal -- except for long
+// causal sequences (8192 keys or more), where the diagonal is a small share
+// of a work item and halving the K/V tile traffic per flop wins.
+template <int D, bool CAUSAL>
+int launch(Args args, hipStream_t stream)
+{
+    if constexpr (D == 128 && CAUSAL) {
+        if (args.Lk >= 8192) return launch_w<D, CAUSAL, 8>(args, stream);
+        return launch_w<D, CAUSAL, 4>(args, stream);
+    } else {
+        return launch_w<D, CAUSAL, (D == 64 ? 4 : 8)>(args, stream);
+    }
 }
 
 }  // namespace
