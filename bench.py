@@ -31,21 +31,23 @@ PEAK_FP16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
 PEAK_FP8_TFLOPS = 5033.2  # dense E4M3: twice the fp16 rate
 PEAK_HBM_GBS = 8000.0  # HBM3E, published
 CSRC = os.path.join(ROOT, "tiled_attention_flash_amd", "csrc")
-KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("fa_device.h", "fa_fwd_kernel.hip",
-                                                 "fa_fwd_fp8_kernel.hip", "fa_splitkv_kernel.hip",
-                                                 "fa_bwd_kernel.hip")]
+# the sources the kernels of each entry point are compiled from
+KERNEL_SRCS = {path: [os.path.join(CSRC, f) for f in ("fa_device.h", "fa_internal.h", src)]
+               for path, src in (("forward", "fa_fwd_kernel.hip"), ("splitkv", "fa_splitkv_kernel.hip"),
+                                 ("backward", "fa_bwd_kernel.hip"), ("fp8", "fa_fwd_fp8_kernel.hip"))}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_sha() -> str:
+def kernel_sha(path: str = "forward") -> str:
+    """Hash of the sources of one entry point's kernels (a workload's `path`)."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
+    for src in KERNEL_SRCS[path]:
+        with open(src, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, path: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, valid
     only while the kernel source is the one the counters were taken on."""
     try:
@@ -54,7 +56,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = data.get(workload)
-    if not entry or entry.get("kernel_sha") != kernel_sha():
+    if not entry or entry.get("kernel_sha") != kernel_sha(path):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -285,7 +287,7 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
 
     value = w.step_flops / (ms_per_step * 1e-3) / 1e12
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name, w.path)
     if w.path == "splitkv":
         # decoding reads each K/V byte once and does ~1 flop per byte: HBM-bound
         achieved = w.algorithmic_bytes / (kernel_ms * 1e-3) / 1e9
@@ -323,7 +325,7 @@ def main() -> int:
         "roofline": roofline,
         "kernel_ms_mean": round(kernel_ms, 5),
         "kernel_ms_median": round(per_launch[len(per_launch) // 2], 5),
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha(w.path),
     }
     print(f"[bench] {name}: {ms_per_step:.4f} ms/step, kernel {kernel_ms:.4f} ms, "
           f"{value:.1f} TFLOP/s ({result['pct_peak']}% of {peak})",
