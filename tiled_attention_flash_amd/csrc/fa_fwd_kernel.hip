@@ -211,7 +211,7 @@ struct Kernel : WaveMath<D, CAUSAL> {
         float rs[2] = {0.0f, 0.0f};
         const float mc = st.mc;
         constexpr int kN = kDBlocks * kCS;
-        constexpr int kVAhead = 4;
+        constexpr int kVAhead = 2;  // measured about 1 % faster than 4
         half8 va[kN];
 
         if constexpr (NEXT) {
