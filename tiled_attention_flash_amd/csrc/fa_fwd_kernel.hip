@@ -45,13 +45,16 @@
 //   of the sequence load row L-1 instead (finite data that the mask hides).
 // * Software pipeline over score blocks of 32 keys: while the matrix unit
 //   computes S of block u+1, the vector ALU exponentiates block u; P.V of
-//   block u then runs beside the row maximum of block u+1.
+//   block u follows.  The wavefront holds a raised issue priority through
+//   the exponential phase, so the other wavefront of its SIMD tends to run
+//   its P.V MFMAs meanwhile.
 // * Online softmax against a reference maximum: block 0 sets each row's
 //   reference to its exact maximum (a row that sees any key sees key 0).
 //   Later blocks are exponentiated against the current reference with no
-//   row maximum of their own; a block whose fp16 probabilities sum to 2^15
-//   or more in some lane (an overflow to inf included) is recomputed after
-//   the reference is raised to the block's maximum and O, l are rescaled.
+//   row maximum of their own; a block whose probabilities sum to 2^15 or
+//   more in some lane (fp32 sums, so an overflow is caught too) is
+//   recomputed after the reference is raised to the block's maximum and
+//   O, l are rescaled.
 //   Kept probabilities stay below 2^15, relative to a weight of 1 that the
 //   row already holds, and the final O / l and LSE are unchanged.
 // * Causal: tiles past the work item's last query are never visited; the
