@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -38,12 +39,18 @@ KERNEL_SRCS = {path: [os.path.join(CSRC, f) for f in ("fa_device.h", "fa_interna
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_sha(path: str = "forward") -> str:
-    """Hash of the sources of one entry point's kernels (a workload's `path`)."""
+    """Hash of the sources of one entry point's kernels (a workload's `path`),
+    with comments and blank lines removed, so that an edit to comments alone
+    keeps the counters taken on the same code."""
     h = hashlib.sha256()
     for src in KERNEL_SRCS[path]:
-        with open(src, "rb") as f:
-            h.update(f.read())
+        with open(src, encoding="utf-8") as f:
+            code = _COMMENT.sub("", f.read())
+        h.update("\n".join(line.rstrip() for line in code.splitlines() if line.strip()).encode())
     return h.hexdigest()[:16]
 
 
