@@ -254,3 +254,42 @@ LONG_CAUSAL_CASES = [
                          ids=[f"q{c[1]}-k{c[2]}-h{c[3]}-kv{c[4]}" for c in LONG_CAUSAL_CASES])
 def test_long_causal_ragged(case):
     test_query_and_key_lengths_differ(case, True)
+
+
+def overrun_inputs(pattern, L, H, D, seed):
+    """Inputs whose scores outgrow the first block's maximum.
+
+    Every query row is the same vector u (|u| = 1) and key j is a multiple of
+    u plus small noise, so the scaled score of key j is about c_j.
+    'rising': c_j grows by 0.3 per key (about 9.6 per 32-key block, far past
+    the 2^15 probability limit), so every later block overruns the reference
+    maximum.  'spike': c_j is small except one key at 60, a single overrun in
+    the middle of the sequence."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(D, generator=g, dtype=torch.float64)
+    u = u / u.norm()
+    scale = 1.0 / np.sqrt(D)
+    if pattern == "rising":
+        c = 0.3 * torch.arange(L, dtype=torch.float64)
+    else:
+        c = torch.zeros(L, dtype=torch.float64)
+        c[L // 2 + 17] = 60.0
+    k = (c / scale)[:, None] * u[None, :] + 0.05 * torch.randn(L, D, generator=g, dtype=torch.float64)
+    q = u.expand(1, L, H, D).clone()
+    k = k[None, :, None, :].expand(1, L, H, D).clone()
+    v = torch.randn(1, L, H, D, generator=g, dtype=torch.float64)
+    return q.half(), k.half(), v.half()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pattern", ["rising", "spike"])
+def test_reference_maximum_overruns(pattern, causal, D):
+    """The path that raises a row's reference maximum and rescales O and l
+    (taken in every block by 'rising', once by 'spike'), element by element
+    against the oracle."""
+    q, k, v = overrun_inputs(pattern, 700, 2, D, seed=11)
+    assert torch.isfinite(k).all()
+    o_ref, lse_ref = oracle.forward(q, k, v, causal=causal)
+    o, lse = gpu_forward(q, k, v, causal)
+    assert_close(o, lse, o_ref, lse_ref, f"overrun {pattern} D={D} causal={causal}")

@@ -134,3 +134,29 @@ def test_splitkv_empty_inputs():
     z = torch.empty((0, 1, 4, 64), dtype=torch.float16, device="cuda")
     o, l = fa.forward_splitkv(z, z, z)
     assert o.shape == z.shape and l.shape == (0, 4, 1)
+
+
+@pytest.mark.parametrize("pattern", ["rising", "spike"])
+def test_splitkv_reference_maximum_overruns(pattern):
+    """Decoding rows whose scores outgrow each split's first block (rising by
+    0.1 per key over 3000 keys), or jump once (one key 60 above the rest):
+    the overrun path inside the splits, then the merge, against the oracle."""
+    D, Lk, Lq, H, Hkv = 128, 3000, 2, 4, 1
+    g = torch.Generator().manual_seed(23)
+    u = torch.randn(D, generator=g, dtype=torch.float64)
+    u = u / u.norm()
+    scale = 1.0 / np.sqrt(D)
+    if pattern == "rising":
+        c = 0.1 * torch.arange(Lk, dtype=torch.float64)
+    else:
+        c = torch.zeros(Lk, dtype=torch.float64)
+        c[1234] = 60.0
+    k = (c / scale)[:, None] * u[None, :] + 0.05 * torch.randn(Lk, D, generator=g, dtype=torch.float64)
+    q = u.expand(1, Lq, H, D).clone().half()
+    k = k[None, :, None, :].clone().half()
+    v = torch.randn(1, Lk, Hkv, D, generator=g, dtype=torch.float64).half()
+    assert torch.isfinite(k).all()
+    o_ref, lse_ref = oracle.forward(q, k, v, causal=True)
+    o, lse = fa.forward_splitkv(q.cuda(), k.cuda(), v.cuda(), causal=True, n_splits=7)
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, lse_ref, f"overrun {pattern}, 7 splits")
