@@ -59,9 +59,10 @@
 //   row already holds, and the final O / l and LSE are unchanged.
 // * Causal: tiles past the work item's last query are never visited; the
 //   mask code runs only on blocks that straddle a wavefront's diagonal (or
-//   hold the ragged end of the sequence).  Blocks past a wavefront's diagonal
-//   but before the work item's end are computed fully masked (weights 0), so
-//   every wavefront runs the same code.
+//   hold the ragged end of the sequence).  A tile whose keys all lie past a
+//   wavefront's last row is skipped by that wavefront, which still issues its
+//   share of the loads and meets the barriers; blocks past its diagonal inside
+//   a tile it does compute are computed fully masked (weights 0).
 // * Grid: one workgroup per (b, kv head, group member, q block) work item;
 //   workgroup ids are remapped so that each of the 8 XCDs (which receive
 //   workgroups round-robin) walks a contiguous range of work items, keeping
@@ -268,6 +269,7 @@ struct Kernel : WaveMath<D, CAUSAL> {
         float c;
         _Float16 (*klds)[G::kTile];
         _Float16 (*vlds)[G::kTile];
+        int wlast;  // causal: key position of the wavefront's last query row
     };
 
     __device__ __forceinline__ static void tile_wait()
@@ -290,6 +292,10 @@ struct Kernel : WaveMath<D, CAUSAL> {
     __device__ __forceinline__ static void tile(State &st, floatx16 &sa, floatx16 &sb, const Ring &r, int t)
     {
         tile_start<P>(r, t);
+        // causal: every key of this and of every later tile lies past the
+        // wavefront's last row, so their weights are all 0 -- the wavefront
+        // only keeps loading and meeting the barriers
+        if (CAUSAL && MASK && kBN * t > r.wlast) return;
         const _Float16 *kl = r.klds[P ^ 1], *vl = r.vlds[P];
         step<true, MASK>(st, sa, sb, kl, vl, kBN * t, r.Lk, r.qp, r.c);
         step<true, MASK>(st, sb, sa, kl + kSB * D, vl + kSB * D, kBN * t + kSB, r.Lk, r.qp, r.c);
@@ -301,6 +307,7 @@ struct Kernel : WaveMath<D, CAUSAL> {
     __device__ __forceinline__ static void tile_final(State &st, floatx16 &sa, floatx16 &sb, const Ring &r, int t)
     {
         tile_wait();
+        if (CAUSAL && MASK && kBN * t > r.wlast) return;
         const _Float16 *kl = r.klds[P ^ 1], *vl = r.vlds[P];
         if (2 * t + 1 < r.n_blocks) {
             step<true, MASK>(st, sa, sb, kl, vl, kBN * t, r.Lk, r.qp, r.c);
@@ -403,7 +410,8 @@ struct Kernel : WaveMath<D, CAUSAL> {
             const float c = a.scale_log2;
 
             // prologue: scores and exact reference maximum of block 0; K tile 0 in flight
-            const Ring r{&lo, kbase, vbase, kv_row, n_tiles, n_blocks, Lk, qp, c, klds, vlds};
+            const int wlast = __builtin_amdgcn_readfirstlane(wq0 + 31 + a.past_len);
+            const Ring r{&lo, kbase, vbase, kv_row, n_tiles, n_blocks, Lk, qp, c, klds, vlds, wlast};
             floatx16 sa, sb;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
