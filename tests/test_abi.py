@@ -227,6 +227,8 @@ def _splits_model(B, Lq, Lk, H, Hkv, D, causal, past_len):
 def test_splitkv_default_splits():
     # hand-checked: 768 resident items at D = 128; 64 items per split -> 12 splits, one round
     assert fa.fa_splitkv_splits(8, 1, 32768, 32, 8, 128, 1, 32767) == 12
+    # 256 items, 128 blocks: three splits fill one round with the least work per split
+    assert fa.fa_splitkv_splits(8, 1, 4096, 32, 32, 128, 1, 4095) == 3
     # one query row of one K/V head over 2^17 keys: capped at 64 splits
     assert fa.fa_splitkv_splits(1, 1, 131072, 32, 8, 128, 1, 131071) == 64
     # 8 blocks: at most 2 splits of >= 4 blocks; 2 blocks: 1
