@@ -134,6 +134,15 @@ def sample_clock_power(step, seconds: float = 1.5, samples: int = 5):
                       "timed region; medians"}
 
 
+def host_cpus() -> dict:
+    """CPUs the host reports and the ones this process may run on."""
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        allowed = os.cpu_count() or 1
+    return {"online": os.cpu_count(), "allowed": allowed}
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -182,7 +191,10 @@ def cpu_baseline(w, q, k, v, target_s: float, descale=None):
     dt = time.perf_counter() - t0
     return {"value": flops(ids) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n} random output rows (b, h, i) of the same inputs, fp64, {dt:.1f} s"}
+            "sample": f"{n} random output rows (b, h, i) of the same inputs, fp64, {dt:.1f} s",
+            "host_cpus": host_cpus(),
+            "threads_note": "oracle threads = the CPUs this process may run on, capped at 16 "
+                            "(the host share of one GPU on a shared box)"}
 
 
 def main() -> int:

@@ -26,3 +26,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    # one line per full-size comparison (max / mean |dO|, max |dLSE|), so the
+    # errors of every workload show in the run's summary, not only on failure
+    lines = []
+    for key in ("passed", "failed"):
+        for rep in terminalreporter.stats.get(key, []):
+            if getattr(rep, "when", "call") != "call":
+                continue
+            for name, value in getattr(rep, "user_properties", []):
+                if name == "parity":
+                    lines.append(("PASS " if key == "passed" else "FAIL ") + str(value))
+    if lines:
+        terminalreporter.write_sep("-", "parity against the fp64 oracle")
+        for line in lines:
+            terminalreporter.write_line(line)

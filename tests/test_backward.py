@@ -147,3 +147,22 @@ def test_backward_rejects_bad_arguments():
     zl = torch.empty((0, 2, 8), dtype=torch.float32, device="cuda")
     r = fa.backward(z, z, z, z, zl, z)
     assert r[0].shape == z.shape
+
+
+def test_backward_rejects_wrong_gradient_buffers():
+    """Caller-supplied dq, dk, dv must match q (dq) or k (dk, dv) in shape,
+    dtype, contiguity and device; anything else is a ValueError raised in the
+    binding before any launch."""
+    q, k, v, do = make_qkvdo(1, 64, 4, 2, 64, seed=1601)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.forward(qd, kd, vd)
+    good_k = torch.empty_like(kd)
+    bad = [dict(dq=torch.empty_like(kd)),                                   # dq shaped like k
+           dict(dq=torch.empty(qd.shape, dtype=torch.float32, device="cuda")),
+           dict(dq=torch.empty((1, 4, 64, 64), dtype=torch.float16, device="cuda").transpose(1, 2)),
+           dict(dk=torch.empty_like(qd)),                                   # dk shaped like q
+           dict(dk=good_k, dv=torch.empty(kd.shape, dtype=torch.float16)),  # dv in host memory
+           dict(dv=torch.empty((1, 32, 2, 64), dtype=torch.float16, device="cuda"))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            fa.backward(qd, kd, vd, o, lse, dod, **kw)

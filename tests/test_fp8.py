@@ -199,3 +199,25 @@ def test_fp8_argument_errors():
     assert e.value.status == 5
     with pytest.raises(TypeError):
         fa.forward_fp8(q8.half(), k8, v8)
+
+
+def test_fp8_rejects_wrong_output_buffers():
+    """A caller's o or lse that does not match q's shape, dtype or device is
+    rejected in the binding, before any launch (the kernel would write
+    B*Lq*H*D fp16 and B*H*Lq fp32 values through them)."""
+    q8, k8, v8, ds = make_qkv_fp8(1, 64, 4, 2, 64, seed=2)
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+    sentinel = torch.full((1, 32, 4, 64), 7.0, dtype=torch.float16, device="cuda")
+    bad_outs = [sentinel,                                                        # too few rows
+                torch.empty((1, 64, 4, 64), dtype=torch.float32, device="cuda"),  # fp32
+                torch.empty((1, 64, 4, 64), dtype=torch.float16)]                 # host memory
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            fa.forward_fp8(q8, k8, v8, descale=ds, out=out)
+    for lse in (torch.empty((1, 4, 32), dtype=torch.float32, device="cuda"),
+                torch.empty((1, 64, 4), dtype=torch.float32, device="cuda"),
+                torch.empty((1, 4, 64), dtype=torch.float16, device="cuda")):
+        with pytest.raises(ValueError):
+            fa.forward_fp8(q8, k8, v8, descale=ds, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)  # nothing was written

@@ -9,11 +9,12 @@ Bar (all absolute, over every compared element):
   grouped-query ratio, both head dims, causal and not -- compared element by
   element.
 * The full-size workloads, in the same launch configuration the benchmark
-  times: rows sampled where errors would show (first/last rows, q-block and
-  key-tile edges, the diagonal neighbourhood, random rows over every head),
-  each computed by the oracle one by one; plus properties that hold at any
-  size (finite output, output inside the range of V, causal row 0 == V[0]
-  exactly, bitwise determinism).
+  times: the whole output of the B=8, H=32, L=1024, D=64 workload (seeds 0-2),
+  and whole (batch, head) slices of the larger ones -- first and last batch,
+  first and last head, and one whole group of grouped query heads -- element
+  by element; rows sampled over every head (q-block and key-tile edges,
+  random rows); and properties that hold at any size (finite output, output
+  inside the range of V, causal row 0 == V[0] exactly, bitwise determinism).
 """
 from __future__ import annotations
 
@@ -44,6 +45,7 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
     assert d.max() <= MAX_O, msg
     assert d.mean() <= MEAN_O, msg
     assert dl.max() <= MAX_LSE, msg
+    return msg
 
 
 def full_case(B, L, H, Hkv, D, causal, seed, qk_mult=1.0):
@@ -110,16 +112,50 @@ def sample_rows(B, H, L, seed, n_random=96):
     return np.array(rows, dtype=np.int64)
 
 
-FULL = ["mha-b8-h32-L1024-d64", "mha-b8-h32-L1024-d64-causal", "mha-b8-h32-L4096-d128",
-        "mha-b8-h32-L4096-d128-causal", "gqa-b2-h32-kv8-L8192-d128-causal",
-        "mha-b1-h32-L16384-d128-causal-qk3", "prefill-b8-h32-q1024-kv4096-d128-causal"]
+# Whole (batch, query head) slices compared element by element at full size.
+# Slices do not interact, so the oracle computes each one exactly on its own
+# Q, K, V slice.  Each list holds the first and last batch and the first and
+# last head, so every q block, every key tile and the last ragged diagonal of
+# both corner sequences are checked; None compares the whole output.
+FULL = {
+    # B=8 H=32 L=1024 D=64 (whole output, seeds 0-2)
+    "mha-b8-h32-L1024-d64": None,
+    "mha-b8-h32-L1024-d64-causal": None,
+    # B=8 H=32 L=4096 D=128
+    "mha-b8-h32-L4096-d128": [(0, 0), (0, 31), (7, 0), (7, 31)],
+    "mha-b8-h32-L4096-d128-causal": [(0, 0), (0, 31), (7, 0), (7, 31)],
+    # GQA B=2 H=32 Hkv=8 L=8192: one whole group of four query heads sharing
+    # K/V head 0, and the corner heads
+    "gqa-b2-h32-kv8-L8192-d128-causal": [(0, 0), (0, 1), (0, 2), (0, 3), (0, 31), (1, 0), (1, 31)],
+    # B=1 H=32 L=16384, Q and K x3: the eight-wavefront causal instance on the
+    # wide logits that take the reference-maximum fixup
+    "mha-b1-h32-L16384-d128-causal-qk3": [(0, 0), (0, 13), (0, 22), (0, 31)],
+    # 1024 queries after 3072 cached keys
+    "prefill-b8-h32-q1024-kv4096-d128-causal": [(0, 0), (0, 31), (7, 0), (7, 31)],
+}
+FULL_CASES = [(name, seed) for name, sl in FULL.items() for seed in ((0, 1, 2) if sl is None else (0,))]
+
+_inputs_cache = {}
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def cached_inputs(name, seed):
+    key = (name, seed)
+    if key not in _inputs_cache:
+        _inputs_cache.clear()  # one workload at a time in host memory
+        _inputs_cache[key] = workload_inputs(WORKLOADS[name], seed=seed)
+    return _inputs_cache[key]
+
+
+@pytest.mark.parametrize("name,seed", FULL_CASES, ids=[f"{n}-seed{s}" for n, s in FULL_CASES])
+def test_full_size(name, seed, record_property):
+    """A full-size workload in the launch configuration the benchmark times:
+    bitwise determinism, properties that hold at any size, sampled rows over
+    every head, and then whole slices (or the whole output) element by
+    element, with max/mean |dO| and max |dLSE| taken over everything
+    compared."""
     w = WORKLOADS[name]
-    print(f"workload {name}", flush=True)
-    q, k, v = workload_inputs(w, seed=0)
+    print(f"workload {name} seed {seed}", flush=True)
+    q, k, v = cached_inputs(name, seed)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o1, lse1 = fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale)
     o2, lse2 = fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale)
@@ -133,12 +169,46 @@ def test_full_size_sampled(name):
     if w.causal and w.past_len == 0:  # row 0 sees only key 0: probability exactly 1
         g = w.H // w.Hkv
         assert torch.equal(o1[:, 0], vd[:, 0].repeat_interleave(g, dim=1))
+    oc, lc = o1.cpu(), lse1.cpu()
+    del o1, o2, lse1, lse2, qd, kd, vd
+
     ids = sample_rows(w.B, w.H, w.L, seed=1)
     o_ref, lse_ref = oracle.rows(q, k, v, ids, causal=w.causal, scale=w.scale)
-    oc, lc = o1.cpu(), lse1.cpu()
     o_got = torch.stack([oc[b, i, h] for b, h, i in ids])
     l_got = torch.stack([lc[b, h, i] for b, h, i in ids])
     assert_close(o_got, l_got, o_ref, lse_ref, f"{name} ({len(ids)} sampled rows)")
+
+    slices = FULL[name]
+    if slices is None:
+        o_ref, lse_ref = oracle.forward(q, k, v, causal=w.causal, scale=w.scale)
+        d = np.abs(oc.double().numpy() - o_ref)
+        dl = np.abs(lc.double().numpy() - lse_ref)
+        what = "whole output"
+        n_elems = d.size
+        dmax, dsum, dlmax = d.max(), d.sum(), dl.max()
+    else:
+        g = w.H // w.Hkv
+        dmax = dsum = dlmax = 0.0
+        n_elems = 0
+        for b, h in slices:
+            hk = h // g
+            qs = q[b:b + 1, :, h:h + 1].contiguous()
+            ks = k[b:b + 1, :, hk:hk + 1].contiguous()
+            vs = v[b:b + 1, :, hk:hk + 1].contiguous()
+            o_ref, lse_ref = oracle.forward(qs, ks, vs, causal=w.causal, scale=w.scale,
+                                            past_len=w.past_len)
+            d = np.abs(oc[b, :, h].double().numpy() - o_ref[0, :, 0])
+            dl = np.abs(lc[b, h].double().numpy() - lse_ref[0, 0])
+            dmax, dsum, dlmax = max(dmax, d.max()), dsum + d.sum(), max(dlmax, dl.max())
+            n_elems += d.size
+        what = f"{len(slices)} whole (b, h) slices"
+    msg = (f"{name} seed {seed}, {what} ({n_elems} elements): max|dO|={dmax:.3e} "
+           f"mean|dO|={dsum / n_elems:.3e} max|dLSE|={dlmax:.3e}")
+    print(msg, flush=True)
+    record_property("parity", msg)
+    assert dmax <= MAX_O, msg
+    assert dsum / n_elems <= MEAN_O, msg
+    assert dlmax <= MAX_LSE, msg
 
 
 # ------------------------------------------------------------- properties
@@ -254,6 +324,17 @@ LONG_CAUSAL_CASES = [
                          ids=[f"q{c[1]}-k{c[2]}-h{c[3]}-kv{c[4]}" for c in LONG_CAUSAL_CASES])
 def test_long_causal_ragged(case):
     test_query_and_key_lengths_differ(case, True)
+
+
+def test_long_causal_wide_logits(record_property):
+    """The eight-wavefront causal instance (8192 keys or more) on Q, K x 3,
+    where rows take the reference-maximum fixup, every element against the
+    oracle: L = 8192 + 75 (ragged), two query heads on one K/V head."""
+    q, k, v = make_qkv(1, 8267, 2, 1, 128, seed=71, qk_mult=3.0)
+    o_ref, lse_ref = oracle.forward(q, k, v, causal=True)
+    o, lse = gpu_forward(q, k, v, True)
+    msg = assert_close(o, lse, o_ref, lse_ref, "L8267 H2 Hkv1 D128 causal, Q,K x3")
+    record_property("parity", msg)
 
 
 def overrun_inputs(pattern, L, H, D, seed):

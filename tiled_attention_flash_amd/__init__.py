@@ -158,9 +158,7 @@ def forward_fp8(q, k, v, descale=(1.0, 1.0, 1.0), causal: bool = False,
     Lk, Hkv = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty((B, L, H, D), dtype=torch.float16, device=q.device)
-    out, lse = _outputs(out, out, lse, with_lse)
+    out, lse = _outputs(q, out, lse, with_lse)
     past = Lk - L if past_len is None else int(past_len)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -189,17 +187,24 @@ def _check_qkv(q, k, v):
 
 
 def _outputs(q, out, lse, with_lse):
+    """Output buffers for a forward over q [B, L, H, D]: the caller's, checked
+    against q's shape and device (o float16, lse float32 [B, H, L]), or new
+    ones.  The kernels write B*L*H*D fp16 values and B*H*L fp32 values, so a
+    smaller or misplaced buffer is rejected here, before any launch."""
     import torch
 
-    B, L, H, _ = q.shape
+    B, L, H, D = q.shape
     if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous float16 tensor shaped like q on q's device")
+        out = torch.empty((B, L, H, D), dtype=torch.float16, device=q.device)
+    elif (not isinstance(out, torch.Tensor) or tuple(out.shape) != (B, L, H, D) or
+          out.dtype != torch.float16 or not out.is_contiguous() or out.device != q.device):
+        raise ValueError("out must be a contiguous float16 [B, L, H, D] tensor shaped like q on "
+                         "q's device")
     if lse is None and with_lse:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (B, H, L) or lse.dtype != torch.float32 or
-                              not lse.is_contiguous() or lse.device != q.device):
+    elif lse is not None and (not isinstance(lse, torch.Tensor) or tuple(lse.shape) != (B, H, L) or
+                              lse.dtype != torch.float32 or not lse.is_contiguous() or
+                              lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 [B, H, L] tensor on q's device")
     return out, lse
 
@@ -270,6 +275,13 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         raise ValueError("lse is required")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    # the kernels write dq like q and dk, dv like k (fp16, BSHD, contiguous)
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t is not None and (not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or
+                              t.shape != like.shape or not t.is_contiguous() or
+                              t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous float16 tensor shaped like "
+                             f"{'q' if like is q else 'k'} on q's device")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
