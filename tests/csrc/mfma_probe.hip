@@ -7,7 +7,9 @@
 //   * v_mfma_f32_32x32x64_f8f6f4 (fp8 e4m3 operands): which A byte meets
 //     which B byte, the result layout, the decoding of every fp8 code;
 //   * ds_read_b64_tr_b8: which LDS bytes each lane receives;
-//   * fp32 -> fp8 e4m3 packed conversion: rounding and byte placement.
+//   * fp32 -> fp8 e4m3 packed conversion: rounding and byte placement;
+//   * v_mfma_f32_4x4x4_16b_f16 (16 independent 4x4x4 blocks): which lanes'
+//     halves meet which, and where each result lands.
 // Test support only; not part of libfa.so.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -18,6 +20,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef int int8v __attribute__((ext_vector_type(8)));
 typedef int int2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
 
 #define PROBE_API extern "C" __attribute__((visibility("default")))
 
@@ -136,5 +140,20 @@ PROBE_API int probe_cvt_fp8(const void *x, void *y, int n, hipStream_t s)
     int n4 = n / 4;
     hipLaunchKernelGGL(cvt_fp8_kernel, dim3((n4 + 255) / 256), dim3(256), 0, s, (const float *)x,
                        (int *)y, n4);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// a, b: [64 lanes][4 halves] as the lanes' operand registers; c: [64][4].
+__global__ void mfma4_kernel(const half4 *a, const half4 *b, float4v *c)
+{
+    int l = threadIdx.x;
+    float4v acc = {};
+    c[l] = __builtin_amdgcn_mfma_f32_4x4x4f16(a[l], b[l], acc, 0, 0, 0);
+}
+
+PROBE_API int probe_mfma_4x4x4_16b_f16(const void *a, const void *b, void *c, hipStream_t s)
+{
+    hipLaunchKernelGGL(mfma4_kernel, dim3(1), dim3(64), 0, s, (const half4 *)a, (const half4 *)b,
+                       (float4v *)c);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -233,3 +233,23 @@ def test_fp8_pack_matches_torch_rounding(probe):
     torch.cuda.synchronize()
     want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(y.cpu().numpy(), want)
+
+
+def test_mfma_4x4x4_16b_ones_sums_own_lane(probe):
+    """v_mfma_f32_4x4x4_16b_f16 with an all-ones A operand: every result
+    register of lane l holds the sum of lane l's own four B halves (each
+    lane's halves are one column of one of the 16 independent blocks, and
+    the result column stays in that lane).  The forward kernel's row sums of
+    the probabilities rely on this."""
+    rng = np.random.default_rng(3)
+    b_lanes = rng.integers(-1000, 1001, size=(64, 4)).astype(np.float16)  # exact sums in fp32
+    a = torch.ones((64, 4), dtype=torch.float16, device="cuda")
+    b = torch.from_numpy(b_lanes).cuda()
+    c = torch.full((64, 4), float("nan"), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert probe.probe_mfma_4x4x4_16b_f16(a.data_ptr(), b.data_ptr(), c.data_ptr(), s) == 0
+    torch.cuda.synchronize()
+    got = c.cpu().numpy()
+    want = b_lanes.astype(np.float64).sum(axis=1)
+    for l in range(64):
+        assert np.all(got[l] == want[l]), (l, got[l], want[l])
