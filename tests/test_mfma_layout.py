@@ -239,8 +239,10 @@ def test_mfma_4x4x4_16b_ones_sums_own_lane(probe):
     """v_mfma_f32_4x4x4_16b_f16 with an all-ones A operand: every result
     register of lane l holds the sum of lane l's own four B halves (each
     lane's halves are one column of one of the 16 independent blocks, and
-    the result column stays in that lane).  The forward kernel's row sums of
-    the probabilities rely on this."""
+    the result column stays in that lane).  A forward variant that took the
+    probabilities' row sums this way was built on this layout and measured
+    (no faster, and its sums carried more error than fp32 adds); the test
+    keeps the layout fact checked."""
     rng = np.random.default_rng(3)
     b_lanes = rng.integers(-1000, 1001, size=(64, 4)).astype(np.float16)  # exact sums in fp32
     a = torch.ones((64, 4), dtype=torch.float16, device="cuda")
