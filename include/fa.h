@@ -77,7 +77,9 @@ enum fa_status {
  *
  * Returns FA_OK once the work is enqueued, or an fa_status error, in which
  * case nothing was launched and no buffer was touched.  All argument checks
- * happen before any HIP call.  B == 0 or L == 0 returns FA_OK and launches
+ * happen before any HIP call.  With causal != 0 the grid is sized to the
+ * workgroups the current device holds at once (its compute units, queried
+ * once per device); FA_ERR_DEVICE if the runtime cannot report them.  B == 0 or L == 0 returns FA_OK and launches
  * nothing.  Faults inside the kernel surface at the caller's next
  * synchronisation on `stream`.
  */

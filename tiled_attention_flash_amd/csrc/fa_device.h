@@ -139,9 +139,9 @@ struct WaveMath {
 
     // LDS read bases for K and V tiles stored row-major (D halves per row)
     // with the k_chunk / v_chunk swizzles, row 0 at the block's first key.
-    __device__ __forceinline__ static void init_lds_bases(State &st)
+    __device__ __forceinline__ static void init_lds_bases(State &st, int lane)
     {
-        const int lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+        const int col = lane & 31, half = lane >> 5;
         // K: row = col, logical chunk 2s + half at k-step s
         st.k_base = col * D + 8 * k_chunk<D>(col, half);
         // V transpose read: 16-lane group gg = lane/16 (d half gg%2, key
@@ -185,13 +185,13 @@ struct WaveMath {
 
     // Mask keys past the end of the keys, and (causal) keys after the query's
     // position qp (its row plus past_len).  Register r holds key
-    // k0 + 4*half + 8(r/4) + r%4, so one per-lane bound decides every element.
-    __device__ __forceinline__ static void mask(floatx16 &sacc, int k0, int Lk, int qp)
+    // k0 + h4 + 8(r/4) + r%4 (h4 = 4 * the lane's half), so one per-lane
+    // bound decides every element.
+    __device__ __forceinline__ static void mask(floatx16 &sacc, int k0, int Lk, int qp, int h4)
     {
-        const int half = (threadIdx.x & 63) >> 5;
-        int bound = Lk - k0 - 4 * half;  // hide offsets >= bound
+        int bound = Lk - k0 - h4;  // hide offsets >= bound
         if (CAUSAL) {
-            const int cb = qp - k0 - 4 * half + 1;
+            const int cb = qp - k0 - h4 + 1;
             bound = cb < bound ? cb : bound;
         }
 #pragma unroll

@@ -65,12 +65,18 @@
 //   a tile it does compute are computed fully masked (weights 0).
 // * Output: O is normalised, rounded to fp16 and exchanged between the two
 //   lane halves so that each lane stores 16 contiguous bytes of its row.
-// * Grid: one workgroup per (b, kv head, group member, q block) work item;
-//   workgroup ids are remapped so that each of the 8 XCDs (which receive
-//   workgroups round-robin) walks a contiguous range of work items, keeping
-//   one head's K/V in that XCD's L2.  Causal q blocks run heaviest first.
+// * Grid, full pass: one workgroup per (b, kv head, group member, q block)
+//   work item; workgroup ids are remapped so that each of the 8 XCDs (which
+//   receive workgroups round-robin) walks a contiguous range of work items,
+//   keeping one head's K/V in that XCD's L2.
+// * Grid, causal: persistent, as the pages' kernel loops over q blocks -- the
+//   resident workgroups walk their XCD's range of units, each unit the pair
+//   of q blocks (nQ-1-i, i) of one row group, so every unit holds equal
+//   work and no workgroup is left with only diagonal-heavy blocks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -87,6 +93,7 @@ struct Args {
     int Lq, Lk;    // query rows, key rows
     int past_len;  // position of query row 0 among the keys (causal mask only)
     int H, Hkv, groups, n_qblocks, n_items;
+    int n_units;  // causal (persistent grid): pairs of q blocks
     float scale;       // multiplier of Q.K
     float scale_log2;  // scale * log2(e): exp(scale*x) == exp2(scale_log2*x)
 };
@@ -103,12 +110,13 @@ struct Geo {
     static_assert(kLoadsPerTile % W == 0, "tile loads must split over the waves");
 };
 
-// Tile row that this lane's n-th direct load fills.
+// Tile row that the n-th direct load of thread tid (lane tid%64 of wave
+// tid/64) fills.
 template <int D, int W>
-__device__ __forceinline__ int load_row(int n)
+__device__ __forceinline__ int load_row(int tid, int n)
 {
     using G = Geo<D, W>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
     return G::kRowsPerLoad * (G::kLoadsPerWave * wave + n) + lane / G::kChunks;
 }
 
@@ -121,13 +129,13 @@ struct LoadOffsets {
 };
 
 template <int D, int W>
-__device__ __forceinline__ void init_load_offsets(LoadOffsets<D, W> &lo, int64_t kv_row)
+__device__ __forceinline__ void init_load_offsets(LoadOffsets<D, W> &lo, int64_t kv_row, int tid)
 {
     using G = Geo<D, W>;
-    const int pc = (threadIdx.x & 63) % G::kChunks;
+    const int pc = (tid & 63) % G::kChunks;
 #pragma unroll
     for (int n = 0; n < G::kLoadsPerWave; ++n) {
-        const int row = load_row<D, W>(n);
+        const int row = load_row<D, W>(tid, n);
         lo.k[n] = (uint32_t)(2 * (row * kv_row + 8 * k_chunk<D>(row, pc)));
         lo.v[n] = (uint32_t)(2 * (row * kv_row + 8 * v_chunk<D>(row, pc)));
     }
@@ -139,10 +147,10 @@ __device__ __forceinline__ void init_load_offsets(LoadOffsets<D, W> &lo, int64_t
 // first K tile starts at key -32) are not loaded and never read.
 template <int D, int W, bool IS_V>
 __device__ __forceinline__ void issue_loads(const LoadOffsets<D, W> &lo, const _Float16 *base,
-                                            int64_t kv_row, int k0, int Lk, _Float16 *lds)
+                                            int64_t kv_row, int k0, int Lk, _Float16 *lds, int tid)
 {
     using G = Geo<D, W>;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const char *tile = (const char *)(base + (int64_t)k0 * kv_row);
     const bool full = k0 + kBN <= Lk;
 #pragma unroll
@@ -151,7 +159,7 @@ __device__ __forceinline__ void issue_loads(const LoadOffsets<D, W> &lo, const _
         if (k0 + G::kRowsPerLoad * blk < 0) continue;  // whole instruction before key 0
         uint32_t off = IS_V ? lo.v[n] : lo.k[n];
         if (!full) {
-            const int over = k0 + load_row<D, W>(n) - (Lk - 1);  // rows past the end re-read row Lk-1
+            const int over = k0 + load_row<D, W>(tid, n) - (Lk - 1);  // rows past the end re-read row Lk-1
             if (over > 0) off -= (uint32_t)(2 * over * kv_row);
         }
         dma16(tile, off, lds + 512 * blk);
@@ -176,6 +184,7 @@ struct Kernel : WaveMath<D, CAUSAL> {
     using M::exp_pair;
     using G = Geo<D, W>;
     static constexpr int kThreads = 64 * W;
+    static constexpr bool kPersistent = CAUSAL;  // see run()
     static constexpr int kBM = 32 * W;  // query rows per work item
 
     // The probabilities of a block overran the limit: raise the reference
@@ -203,9 +212,9 @@ struct Kernel : WaveMath<D, CAUSAL> {
     template <bool NEXT, bool MASK>
     __device__ __forceinline__ static void step(State &st, floatx16 &sc, floatx16 &sn,
                                                 const _Float16 *kl, const _Float16 *vl, int k0,
-                                                int Lk, int qp, float c)
+                                                int Lk, int qp, int h4, float c)
     {
-        if constexpr (MASK) mask(sc, k0, Lk, qp);
+        if constexpr (MASK) mask(sc, k0, Lk, qp, h4);
         // The two wavefronts that share a SIMD run best in opposite phases:
         // one exponentiating (vector ALU and matrix unit) while the other
         // feeds the matrix unit with its P.V products.  A wavefront raises
@@ -268,6 +277,8 @@ struct Kernel : WaveMath<D, CAUSAL> {
         const _Float16 *kbase, *vbase;
         int64_t kv_row;
         int n_tiles, n_blocks, Lk, qp;
+        int h4;  // 4 * (lane / 32): key offset of the lane's half in a score block
+        int tid;
         float c;
         _Float16 (*klds)[G::kTile];
         _Float16 (*vlds)[G::kTile];
@@ -285,8 +296,9 @@ struct Kernel : WaveMath<D, CAUSAL> {
     {
         tile_wait();
         if (2 * t + 3 < r.n_blocks)
-            issue_loads<D, W, false>(*r.lo, r.kbase, r.kv_row, kBN * (t + 1) + kSB, r.Lk, r.klds[P]);
-        if (t + 1 < r.n_tiles) issue_loads<D, W, true>(*r.lo, r.vbase, r.kv_row, kBN * (t + 1), r.Lk, r.vlds[P ^ 1]);
+            issue_loads<D, W, false>(*r.lo, r.kbase, r.kv_row, kBN * (t + 1) + kSB, r.Lk, r.klds[P], r.tid);
+        if (t + 1 < r.n_tiles)
+            issue_loads<D, W, true>(*r.lo, r.vbase, r.kv_row, kBN * (t + 1), r.Lk, r.vlds[P ^ 1], r.tid);
     }
 
     // a tile whose two blocks both have a successor; MASK: mask both blocks
@@ -299,8 +311,8 @@ struct Kernel : WaveMath<D, CAUSAL> {
         // only keeps loading and meeting the barriers
         if (CAUSAL && MASK && kBN * t > r.wlast) return;
         const _Float16 *kl = r.klds[P ^ 1], *vl = r.vlds[P];
-        step<true, MASK>(st, sa, sb, kl, vl, kBN * t, r.Lk, r.qp, r.c);
-        step<true, MASK>(st, sb, sa, kl + kSB * D, vl + kSB * D, kBN * t + kSB, r.Lk, r.qp, r.c);
+        step<true, MASK>(st, sa, sb, kl, vl, kBN * t, r.Lk, r.qp, r.h4, r.c);
+        step<true, MASK>(st, sb, sa, kl + kSB * D, vl + kSB * D, kBN * t + kSB, r.Lk, r.qp, r.h4, r.c);
     }
 
     // the final tile (t = n_tiles - 1): block 2t+1, if it exists, is the
@@ -312,10 +324,10 @@ struct Kernel : WaveMath<D, CAUSAL> {
         if (CAUSAL && MASK && kBN * t > r.wlast) return;
         const _Float16 *kl = r.klds[P ^ 1], *vl = r.vlds[P];
         if (2 * t + 1 < r.n_blocks) {
-            step<true, MASK>(st, sa, sb, kl, vl, kBN * t, r.Lk, r.qp, r.c);
-            step<false, MASK>(st, sb, sa, nullptr, vl + kSB * D, kBN * t + kSB, r.Lk, r.qp, r.c);
+            step<true, MASK>(st, sa, sb, kl, vl, kBN * t, r.Lk, r.qp, r.h4, r.c);
+            step<false, MASK>(st, sb, sa, nullptr, vl + kSB * D, kBN * t + kSB, r.Lk, r.qp, r.h4, r.c);
         } else {
-            step<false, MASK>(st, sa, sb, nullptr, vl, kBN * t, r.Lk, r.qp, r.c);
+            step<false, MASK>(st, sa, sb, nullptr, vl, kBN * t, r.Lk, r.qp, r.h4, r.c);
         }
     }
 
@@ -346,26 +358,19 @@ struct Kernel : WaveMath<D, CAUSAL> {
         else tile_final<0, MASK>(st, sa, sb, r, t);
     }
 
-    __device__ static void run(const Args &a)
+    // One work item: q block qb of query head h (K/V head hk) of batch b.
+    __device__ __forceinline__ static void item(const Args &a, int b, int hk, int h, int qb,
+                                                _Float16 (*klds)[G::kTile], _Float16 (*vlds)[G::kTile])
     {
-        __shared__ __attribute__((aligned(16))) _Float16 klds[2][G::kTile];
-        __shared__ __attribute__((aligned(16))) _Float16 vlds[2][G::kTile];
-
-        const int tid = threadIdx.x;
+        // In the persistent loop the thread id passes through an empty asm
+        // statement once per work item, so everything derived from it is
+        // computed inside the loop of `run` rather than hoisted out of it and
+        // kept live (and spilled) across the whole loop.
+        int tid = threadIdx.x;
+        if constexpr (kPersistent) __asm__ volatile("" : "+v"(tid));
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int col = lane & 31, half = lane >> 5;
-
-        // ---- work item
-        const int item = xcd_item(blockIdx.x, a.n_items);
-        int rest = item / a.n_qblocks;
-        int qb = item % a.n_qblocks;
-        if (CAUSAL) qb = a.n_qblocks - 1 - qb;  // heaviest blocks first
-        const int g = rest % a.groups;
-        rest /= a.groups;
-        const int hk = rest % a.Hkv;
-        const int b = rest / a.Hkv;
-        const int h = hk * a.groups + g;
         const int Lq = a.Lq, Lk = a.Lk;
         const int q0 = qb * kBM;
 
@@ -398,9 +403,9 @@ struct Kernel : WaveMath<D, CAUSAL> {
             // K tile -1 (keys 0..31 in its upper half) and V tile 0 in flight
             // while Q is fetched
             LoadOffsets<D, W> lo;
-            init_load_offsets<D, W>(lo, kv_row);
-            issue_loads<D, W, false>(lo, kbase, kv_row, -kSB, Lk, klds[0]);
-            issue_loads<D, W, true>(lo, vbase, kv_row, 0, Lk, vlds[0]);
+            init_load_offsets<D, W>(lo, kv_row, tid);
+            issue_loads<D, W, false>(lo, kbase, kv_row, -kSB, Lk, klds[0], tid);
+            issue_loads<D, W, true>(lo, vbase, kv_row, 0, Lk, vlds[0], tid);
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
                 half8 val = {};
@@ -408,18 +413,18 @@ struct Kernel : WaveMath<D, CAUSAL> {
                 st.qf[s] = val;
             }
             // K row = col (+ 32 for the upper half of a tile)
-            M::init_lds_bases(st);
+            M::init_lds_bases(st, lane);
             const float c = a.scale_log2;
 
             // prologue: scores and exact reference maximum of block 0; K tile 0 in flight
             const int wlast = __builtin_amdgcn_readfirstlane(wq0 + 31 + a.past_len);
-            const Ring r{&lo, kbase, vbase, kv_row, n_tiles, n_blocks, Lk, qp, c, klds, vlds, wlast};
+            const Ring r{&lo, kbase, vbase, kv_row, n_tiles, n_blocks, Lk, qp, 4 * half, tid, c, klds, vlds, wlast};
             floatx16 sa, sb;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (n_blocks > 1) issue_loads<D, W, false>(lo, kbase, kv_row, kSB, Lk, klds[1]);
+            if (n_blocks > 1) issue_loads<D, W, false>(lo, kbase, kv_row, kSB, Lk, klds[1], tid);
             s_product(sa, st, klds[0] + kSB * D);
-            mask(sa, 0, Lk, qp);
+            mask(sa, 0, Lk, qp, 4 * half);
             rescale(st, block_max(sa), c);
 
             // Tiles t < n_main have a successor for both blocks; tile
@@ -488,6 +493,59 @@ struct Kernel : WaveMath<D, CAUSAL> {
                 a.lse[((int64_t)b * a.H + h) * Lq + qi] = st.m * a.scale + __logf(lt);
         }
     }
+
+    // Row group r = (b * Hkv + hk) * groups + g -> batch, K/V head, query head.
+    __device__ __forceinline__ static void decode(const Args &a, int r, int &b, int &hk, int &h)
+    {
+        const int g = r % a.groups;
+        r /= a.groups;
+        hk = r % a.Hkv;
+        b = r / a.Hkv;
+        h = hk * a.groups + g;
+    }
+
+    // Work decomposition.
+    //  * Full pass: one workgroup per work item, xcd_item(blockIdx.x).
+    //  * Causal (the loop of the pages' kernel over q blocks): persistent.  The
+    //    grid is the resident workgroups, a multiple of 8.  The units are
+    //    pairs of q blocks (nQ-1-i, i) of one row group, so that every unit
+    //    holds the same work (with past_len p and blocks of BM rows the pair
+    //    sees 2p + (nQ+1)BM keys in all).  They are cut into 8 contiguous
+    //    ranges, one per XCD (workgroups reach the XCDs round robin), and the
+    //    workgroups of an XCD take the units of its range in turn, the heavy
+    //    block of a pair first; a barrier separates consecutive items, whose
+    //    first loads reuse the LDS tiles.
+    __device__ static void run(const Args &a)
+    {
+        __shared__ __attribute__((aligned(16))) _Float16 klds[2][G::kTile];
+        __shared__ __attribute__((aligned(16))) _Float16 vlds[2][G::kTile];
+        const int nq = a.n_qblocks;
+        if constexpr (!kPersistent) {
+            const int it = xcd_item(blockIdx.x, a.n_items);
+            int b, hk, h;
+            decode(a, it / nq, b, hk, h);
+            item(a, b, hk, h, it % nq, klds, vlds);
+        } else {
+            const int x = blockIdx.x % kXcds, per = a.n_units / kXcds, extra = a.n_units % kXcds;
+            const int first = x * per + (x < extra ? x : extra);
+            const int end = first + per + (x < extra ? 1 : 0);
+            const int stride = (int)gridDim.x / kXcds;
+            const int upg = (nq + 1) / 2;  // units (pairs) per row group
+            bool started = false;
+            for (int u = first + (int)blockIdx.x / kXcds; u < end; u += stride) {
+                const int i = u % upg;
+                int b, hk, h;
+                decode(a, u / upg, b, hk, h);
+                for (int j = 0; j < 2; ++j) {
+                    const int qb = j == 0 ? nq - 1 - i : i;
+                    if (j == 1 && qb == nq - 1 - i) break;  // middle block of an odd count
+                    if (started) __syncthreads();  // every wavefront is done with the LDS tiles
+                    started = true;
+                    item(a, b, hk, h, qb, klds, vlds);
+                }
+            }
+        }
+    }
 };
 
 // Wavefronts per SIMD: 2 at D = 128 (about 248 VGPRs each); 3 at D = 64,
@@ -502,6 +560,38 @@ fa_fwd_kernel(const Args a)
     Kernel<D, CAUSAL, W>::run(a);
 }
 
+// Workgroups of `kernel` (with `threads` threads) resident on the whole
+// current device at once: compute units x workgroups per compute unit (from
+// the kernel's registers and LDS).  Queried once per device and kernel; 0 if
+// the runtime cannot say.
+int resident_workgroups(const void *kernel, int threads)
+{
+    constexpr int kMaxDevices = 64, kMaxKernels = 8;
+    static std::atomic<int> cache[kMaxDevices][kMaxKernels];
+    static std::atomic<const void *> keys[kMaxKernels];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    int slot = -1;
+    for (int i = 0; i < kMaxKernels && slot < 0; ++i) {
+        const void *cur = keys[i].load();
+        if (cur == kernel) slot = i;
+        else if (cur == nullptr) {
+            const void *expected = nullptr;
+            if (keys[i].compare_exchange_strong(expected, kernel) || expected == kernel) slot = i;
+        }
+    }
+    if (slot >= 0 && dev < kMaxDevices) {
+        const int v = cache[dev][slot].load();
+        if (v > 0) return v;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+    const int v = cus > 0 && per_cu > 0 ? cus * per_cu : 0;
+    if (slot >= 0 && dev < kMaxDevices && v > 0) cache[dev][slot].store(v);
+    return v;
+}
+
 template <int D, bool CAUSAL, int W>
 int launch_w(Args args, hipStream_t stream)
 {
@@ -509,9 +599,21 @@ int launch_w(Args args, hipStream_t stream)
     args.n_qblocks = (args.Lq + K::kBM - 1) / K::kBM;
     const int64_t items = (int64_t)args.n_items * args.n_qblocks;  // n_items holds B*H here
     if (items > 0x7fffffff) return FA_ERR_SHAPE;
+    const int rows = args.n_items;
     args.n_items = (int)items;
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, W>), dim3(args.n_items), dim3(K::kThreads), 0,
-                       stream, args);
+    int grid = args.n_items;
+    args.n_units = 0;
+    if (K::kPersistent) {
+        const int slots = resident_workgroups((const void *)fa_fwd_kernel<D, CAUSAL, W>, K::kThreads);
+        if (slots <= 0) return FA_ERR_DEVICE;
+        const int64_t units = (int64_t)rows * ((args.n_qblocks + 1) / 2);
+        args.n_units = (int)units;  // <= items
+        // a multiple of 8, so that blockIdx.x % 8 names the XCD for every slot
+        const int64_t want = units < slots ? units : slots;
+        grid = (int)((want + kXcds - 1) / kXcds * kXcds);
+    }
+    if (grid == 0) return FA_OK;
+    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, W>), dim3(grid), dim3(K::kThreads), 0, stream, args);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

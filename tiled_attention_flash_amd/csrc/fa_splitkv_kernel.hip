@@ -165,7 +165,7 @@ struct SplitKernel : WaveMath<D, CAUSAL> {
     {
         floatx16 s;
         M::s_product(s, st, kl);
-        if (M::needs_mask(k0, Lk, wp0)) M::mask(s, k0, Lk, qp);
+        if (M::needs_mask(k0, Lk, wp0)) M::mask(s, k0, Lk, qp, 4 * ((int)(threadIdx.x & 63) >> 5));
         M::rescale(st, M::block_max(s), c);
         half8 pf[M::kCS];
         float rs[2] = {0.0f, 0.0f};
@@ -238,7 +238,7 @@ struct SplitKernel : WaveMath<D, CAUSAL> {
             // rather than a compiler-placed one for Q inside the loop, which
             // would also drain the ring every iteration
             wait_vmcnt<0>();
-            M::init_lds_bases(st);
+            M::init_lds_bases(st, (int)threadIdx.x & 63);
             const float c = a.scale_log2;
 
             int stage = 0;  // ring stage of block t
