@@ -197,6 +197,83 @@ def cpu_baseline(w, q, k, v, target_s: float, descale=None):
                             "(the host share of one GPU on a shared box)"}
 
 
+def run_probe(args) -> int:
+    """The reference ceilings: a register-only stream of v_mfma_f32_32x32x16_f16
+    (four independent chains per wavefront, two wavefronts per SIMD), or one
+    streaming read of a device buffer (16 bytes per lane, grid-strided).
+    Same timing as the workloads: warmup, then `--steps` launches between HIP
+    events on the launch stream; clock and power sampled afterwards while the
+    same launches run."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "tiled_attention_flash_amd", "libfa_clock.so")
+    if not os.path.exists(path):
+        print(f"{path} is not built", file=sys.stderr)
+        return 1
+    lib = ctypes.CDLL(path)
+    lib.fa_probe_mfma_stream.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p,
+                                         ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_mfma_stream.restype = lib.fa_probe_read_stream.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if args.mfma_probe:
+        workgroups, iters = 8 * cus, 512  # 8 rounds of one 8-wavefront workgroup per CU
+        structured = int(args.mfma_probe == "structured")
+        out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+        work = workgroups * 8 * iters * 32 * 32768.0  # flops per launch
+
+        def step():
+            if lib.fa_probe_mfma_stream(out.data_ptr(), out.numel(), workgroups, iters, structured,
+                                        stream.cuda_stream) != 0:
+                raise RuntimeError("fa_probe_mfma_stream rejected")
+        name, unit, peak = f"mfma_stream_f16_{args.mfma_probe}", "TFLOP/s", PEAK_FP16_TFLOPS
+    else:
+        nbytes = args.read_probe_mib * (1 << 20)
+        buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        workgroups = 16 * cus
+        out = torch.empty(workgroups * 256, dtype=torch.int32, device=dev)
+        work = float(nbytes)  # bytes per launch
+
+        def step():
+            if lib.fa_probe_read_stream(buf.data_ptr(), nbytes, out.data_ptr(), out.numel(),
+                                        workgroups, stream.cuda_stream) != 0:
+                raise RuntimeError("fa_probe_read_stream rejected")
+        name, unit, peak = "read_stream", "GB/s", PEAK_HBM_GBS
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = t0.elapsed_time(t1) / args.steps
+    rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+    result = {"probe": name, "value": round(rate, 1), "unit": unit, "peak": peak,
+              "frac_of_peak": round(rate / peak, 4), "ms_per_launch": round(ms, 4),
+              "steps": args.steps, "warmup": args.warmup, "compute_units": cus,
+              "workgroups": workgroups}
+    if args.mfma_probe:
+        result["flops_per_launch"] = work
+    else:
+        result["bytes_per_launch"] = int(work)
+    clock = sample_clock_power(step)
+    if clock and unit == "TFLOP/s" and (clock["gfxclk_mhz"] or 0) >= 500:
+        clock["peak_at_clock_tflops"] = round(peak * clock["gfxclk_mhz"] / 2400.0, 1)
+        clock["frac_at_clock"] = round(rate / clock["peak_at_clock_tflops"], 4)
+    result["clock"] = clock
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +286,13 @@ def main() -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB "
                          "`--steps` times (the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--mfma-probe", choices=["random", "structured"], default=None,
+                    help="instead of the benchmark, time the register-only fp16 MFMA stream of "
+                         "libfa_clock.so on random operands (the sustained matrix-unit ceiling "
+                         "for data like the workloads') or on few distinct small values")
+    ap.add_argument("--read-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, time a streaming read of this many MiB of "
+                         "device memory (libfa_clock.so): the practical HBM read ceiling")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -229,6 +313,9 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n,
                           "launches": args.steps}), flush=True)
         return 0
+
+    if args.mfma_probe or args.read_probe_mib:
+        return run_probe(args)
 
     import tiled_attention_flash_amd as fa
     from tiled_attention_flash_amd.inputs import HEADLINE, WORKLOADS, workload_inputs

@@ -1,5 +1,8 @@
-// fa_clock_probe.hip -- measurement helper for the benchmark (libfa_clock.so),
-// not part of the attention library.
+// fa_clock_probe.hip -- measurement helpers for the benchmark (libfa_clock.so),
+// not part of the attention library: the shader clock probe, and two
+// reference kernels that give the ceilings the attention kernels are judged
+// against on this part -- a register-only stream of fp16 matrix
+// instructions, and a streaming read of device memory.
 //
 // The shader clock the GPU actually runs at while a workload executes: one
 // wavefront, launched on a side stream while the workload's kernels are in
@@ -24,7 +27,113 @@ __global__ void clock_probe_kernel(unsigned long long *out, unsigned long long w
     out[1] = r1 - r0;
 }
 
+typedef _Float16 half8p __attribute__((ext_vector_type(8)));
+typedef float floatx16p __attribute__((ext_vector_type(16)));
+typedef unsigned int uint4p __attribute__((ext_vector_type(4)));
+
+// Four independent accumulator chains of v_mfma_f32_32x32x16_f16 per
+// wavefront, operands held in registers, eight wavefronts per workgroup and
+// two per SIMD (the occupancy of the attention kernels at D = 128): the
+// matrix unit's sustained fp16 rate with no memory traffic at all.  The
+// matrix unit's power, and so the clock the part holds under its power
+// limit, depends on the operand bits: by default every operand is an fp16
+// value with a random sign, a random 10-bit fraction and a magnitude in
+// [1/4, 4) (an xorshift stream per lane), and the four chains rotate through
+// eight such A and B fragments, as a kernel multiplying Gaussian data sees;
+// `structured` instead uses few distinct small values (many zeros), which
+// draws much less power.  Each thread writes one sum at the end so the
+// chains are not removed.
+__device__ __forceinline__ unsigned int xorshift(unsigned int &x)
+{
+    x ^= x << 13;
+    x ^= x >> 17;
+    x ^= x << 5;
+    return x;
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
+mfma_stream_kernel(float *out, int iters, int structured)
+{
+    const int t = threadIdx.x;
+    half8p A[8], B[8];
+    unsigned int x = 0x9e3779b9u ^ (unsigned int)((blockIdx.x * blockDim.x + t) * 2654435761u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (structured) {
+                A[j][i] = (_Float16)(((t + i + j) & 7) * 0.0625f);
+                B[j][i] = (_Float16)(((t * 3 + i + j) & 7) * 0.0625f);
+            } else {
+                // sign, exponent 13..16 (2^-2 .. 2^1), fraction: binary16 bits
+                const unsigned int ra = xorshift(x), rb = xorshift(x);
+                const unsigned short ha = (unsigned short)(((ra >> 15) & 0x8000u) | ((13u + (ra & 3u)) << 10) |
+                                                           ((ra >> 2) & 0x3ffu));
+                const unsigned short hb = (unsigned short)(((rb >> 15) & 0x8000u) | ((13u + (rb & 3u)) << 10) |
+                                                           ((rb >> 2) & 0x3ffu));
+                A[j][i] = __builtin_bit_cast(_Float16, ha);
+                B[j][i] = __builtin_bit_cast(_Float16, hb);
+            }
+        }
+    floatx16p c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[j], B[j], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[j], B[(j + 3) & 7], c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 5) & 7], B[j], c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 2) & 7], B[(j + 6) & 7], c3, 0, 0, 0);
+        }
+    }
+    float s = 0.0f;
+    for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+    out[(size_t)blockIdx.x * blockDim.x + t] = s;
+}
+
+// Streaming read: every thread loads 16 bytes per step, grid-strided over
+// n16 16-byte elements (the whole buffer, once), and writes one word.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void
+read_stream_kernel(const uint4p *buf, size_t n16, unsigned int *out)
+{
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t step = (size_t)gridDim.x * blockDim.x;
+    uint4p acc = {0u, 0u, 0u, 0u};
+    for (size_t i = gid; i < n16; i += step) acc ^= buf[i];
+    out[gid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 }  // namespace
+
+// Matrix-unit ceiling: `workgroups` workgroups of 512 threads, each wavefront
+// issuing 32 * iters v_mfma_f32_32x32x16_f16 (32768 flops each); random
+// operands, or few distinct small values when `structured` is nonzero.  out:
+// device buffer of at least workgroups * 512 floats.  Returns 0, or 1 on bad
+// arguments or a rejected launch.
+extern "C" __attribute__((visibility("default"))) int fa_probe_mfma_stream(void *out, long long out_floats,
+                                                                            int workgroups, int iters,
+                                                                            int structured, void *stream)
+{
+    if (!out || workgroups <= 0 || iters <= 0 || out_floats < (long long)workgroups * 512) return 1;
+    hipLaunchKernelGGL(mfma_stream_kernel, dim3(workgroups), dim3(512), 0, (hipStream_t)stream,
+                       (float *)out, iters, structured);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// Read ceiling: `workgroups` workgroups of 256 threads read the `bytes` bytes
+// at buf (a multiple of 16, 16-byte aligned) once; out: device buffer of at
+// least workgroups * 256 words.  Returns 0, or 1 on bad arguments or a
+// rejected launch.
+extern "C" __attribute__((visibility("default"))) int fa_probe_read_stream(const void *buf, long long bytes,
+                                                                            void *out, long long out_words,
+                                                                            int workgroups, void *stream)
+{
+    if (!buf || !out || bytes <= 0 || (bytes & 15) || ((uintptr_t)buf & 15) || workgroups <= 0 ||
+        out_words < (long long)workgroups * 256)
+        return 1;
+    hipLaunchKernelGGL(read_stream_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4p *)buf, (size_t)(bytes / 16), (unsigned int *)out);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 
 // out: device buffer of 2 uint64 (shader cycles, 100 MHz ticks) written by
 // the probe; window_ticks: window length in 100 MHz ticks (>= 1); stream:
