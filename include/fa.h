@@ -49,9 +49,14 @@ enum fa_status {
     FA_ERR_ALIAS = 7,    /* the byte range of o or lse overlaps q, k, v or each other */
     FA_ERR_LAUNCH = 8,   /* the HIP runtime rejected the launch                    */
     FA_ERR_DEVICE = 9,   /* the current device could not be queried                */
-    FA_ERR_WORKSPACE = 10 /* fa_fwd_splitkv: workspace NULL, too small or not
+    FA_ERR_WORKSPACE = 10, /* fa_fwd_splitkv: workspace NULL, too small or not
                              16-byte aligned                                       */
+    FA_ERR_SCRATCH = 11   /* fa_fwd_splitkv_noalloc: the partial results need more
+                             than FA_SPLITKV_SCRATCH_BYTES                         */
 };
+
+/* Size of the static device scratch of fa_fwd_splitkv_noalloc (16 MiB). */
+#define FA_SPLITKV_SCRATCH_BYTES (16LL << 20)
 
 /*
  * fa_fwd -- attention forward pass.
@@ -193,6 +198,32 @@ FA_API int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, 
                           float scale, int n_splits, void *workspace, long long workspace_bytes,
                           hipStream_t stream);
 
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  It allocates
+ * nothing: the partial results go to a static device array of
+ * FA_SPLITKV_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  Same kernels, same results (bitwise) as
+ * fa_fwd_splitkv with the same n_splits.
+ *
+ * Arguments and errors as for fa_fwd_splitkv, without workspace and
+ * workspace_bytes; in addition FA_ERR_SCRATCH (checked before any HIP call)
+ * when fa_splitkv_workspace_bytes(B, Lq, H, D, n_splits) exceeds
+ * FA_SPLITKV_SCRATCH_BYTES -- pass fewer splits, or use fa_fwd_splitkv --
+ * and FA_ERR_DEVICE if the scratch's device address cannot be obtained.
+ *
+ * Every call on one GPU uses that GPU's one scratch array: calls that may
+ * run concurrently on one GPU (on different streams, or from several host
+ * threads without ordering) race on it and must not overlap.  Calls ordered
+ * on one stream are safe.  Nothing in the scratch needs to start at zero;
+ * each call overwrites what it reads.
+ */
+FA_API int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o,
+                                  float *lse, int B, int Lq, int Lk, int H, int Hkv, int D,
+                                  int causal, int past_len, float scale, int n_splits,
+                                  hipStream_t stream);
+
 /* The number of key splits fa_fwd_splitkv uses when passed n_splits = 0.
  * Work items (one wavefront per row block and split) run in rounds of as
  * many as the GPU holds at once (256 compute units x 160 KiB of LDS over
@@ -248,7 +279,7 @@ FA_API const char *fa_status_string(int status);
 /* Version of this ABI (bumped when an entry point is added or a signature or
  * a layout changes): 2 = fa_fwd, fa_fwd_kv; 3 adds fa_fwd_splitkv,
  * fa_splitkv_splits and fa_splitkv_workspace_bytes; 4 adds fa_bwd; 5 adds
- * fa_fwd_fp8. */
+ * fa_fwd_fp8; 6 adds fa_fwd_splitkv_noalloc. */
 FA_API int fa_abi_version(void);
 
 #ifdef __cplusplus

@@ -36,8 +36,9 @@ def test_library_loads_and_exports_header_symbols():
     lib = fa.library()
     names = declared_symbols()
     assert set(names) == {"fa_fwd", "fa_fwd_kv", "fa_fwd_fp8", "fa_fwd_splitkv",
-                          "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_bwd",
-                          "fa_status_string", "fa_abi_version"}
+                          "fa_fwd_splitkv_noalloc", "fa_splitkv_splits",
+                          "fa_splitkv_workspace_bytes", "fa_bwd", "fa_status_string",
+                          "fa_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], check=True,
                          stdout=subprocess.PIPE, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -46,7 +47,7 @@ def test_library_loads_and_exports_header_symbols():
         assert hasattr(lib, n)
     # nothing beyond the declared C ABI leaks out of the library
     assert exported == set(names)
-    assert lib.fa_abi_version() == 5
+    assert lib.fa_abi_version() == 6
 
 
 def test_status_strings():
@@ -270,6 +271,45 @@ def test_splitkv_exact_workspace_size_accepted_by_validation():
     assert call_split(Lq=0, workspace=None, workspace_bytes=0) == 0
     assert call_split(B=0, workspace=None, workspace_bytes=0) == 0
     assert call_split(B=0, n_splits=5000) == 2  # still validated
+
+
+def call_noalloc(**kw):
+    a = dict(SPLIT_ARGS)
+    a.update(kw)
+    return fa.fa_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Lq"],
+                                     a["Lk"], a["H"], a["Hkv"], a["D"], a["causal"],
+                                     a["past_len"], a["scale"], a["n_splits"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(Lk=-1), 2), (dict(H=3, Hkv=2), 3),
+    (dict(D=96), 4), (dict(scale=math.nan), 5), (dict(v=V + 2), 6), (dict(o=Q), 7),
+    (dict(n_splits=-1), 2), (dict(n_splits=4097), 2),
+])
+def test_splitkv_noalloc_invalid_arguments_rejected_without_launch(kw, status):
+    assert call_noalloc(**kw) == status
+
+
+def test_splitkv_noalloc_rejects_problems_beyond_its_scratch():
+    """Partial results larger than the static scratch (16 MiB) are refused
+    with FA_ERR_SCRATCH before any HIP call; the limit is exact."""
+    assert fa.SPLITKV_SCRATCH_BYTES == 16 << 20
+    # B*H*Lq*n*(D+1)*4 bytes: 8 query rows of 2 heads over 4096 splits need 17 MB
+    assert fa.fa_splitkv_workspace_bytes(1, 8, 2, 64, 4096) > fa.SPLITKV_SCRATCH_BYTES
+    assert call_noalloc(Lq=8, past_len=4088, n_splits=4096) == 11
+    # the largest n_splits that still fits a B=8, H=32, Lq=1, D=128 decode step
+    need = lambda n: fa.fa_splitkv_workspace_bytes(8, 1, 32, 128, n)  # noqa: E731
+    n_fit = max(n for n in range(1, 4097) if need(n) <= fa.SPLITKV_SCRATCH_BYTES)
+    assert need(n_fit + 1) > fa.SPLITKV_SCRATCH_BYTES
+    big = dict(SPLIT_ARGS, B=8, H=32, Hkv=8, Lq=1, D=128, past_len=4095)
+    assert call_noalloc(**dict(big, n_splits=n_fit + 1)) == 11
+    assert "FA_ERR_SCRATCH" in fa.fa_status_string(11)
+
+
+def test_splitkv_noalloc_empty_problems_are_noops():
+    assert call_noalloc(Lq=0) == 0
+    assert call_noalloc(B=0) == 0
+    assert call_noalloc(B=0, n_splits=5000) == 2  # still validated
 
 
 # ------------------------------------------------------------ backward ABI

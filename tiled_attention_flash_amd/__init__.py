@@ -18,6 +18,8 @@ Lk - Lq, which the causal mask uses.
 computes the same result by splitting the keys over separate wavefronts and
 merging the partial results (for few query rows against many keys); its fp32
 workspace is allocated with torch unless one is passed.
+``forward_splitkv_noalloc`` does the same with the library's static device
+scratch instead of a workspace (for callers that cannot allocate).
 
     o, lse = tiled_attention_flash_amd.forward_fp8(q8, k8, v8, descale=(qd, kd, vd))
 
@@ -33,8 +35,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["forward", "forward_splitkv", "forward_fp8", "backward", "fa_fwd", "fa_fwd_kv",
-           "fa_fwd_splitkv", "fa_fwd_fp8", "fa_bwd",
+__all__ = ["forward", "forward_splitkv", "forward_splitkv_noalloc", "forward_fp8", "backward",
+           "fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_fwd_fp8", "fa_bwd",
            "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_status_string", "library",
            "library_path", "FaError", "STATUS"]
 
@@ -45,8 +47,10 @@ _lib = None
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_SHAPE", 3: "FA_ERR_GQA", 4: "FA_ERR_HEADDIM",
     5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS", 8: "FA_ERR_LAUNCH",
-    9: "FA_ERR_DEVICE", 10: "FA_ERR_WORKSPACE",
+    9: "FA_ERR_DEVICE", 10: "FA_ERR_WORKSPACE", 11: "FA_ERR_SCRATCH",
 }
+
+SPLITKV_SCRATCH_BYTES = 16 << 20  # FA_SPLITKV_SCRATCH_BYTES
 
 
 class FaError(RuntimeError):
@@ -76,6 +80,8 @@ def library():
     lib.fa_fwd_splitkv.argtypes = ([vp, vp, vp, vp, vp] + [c_int] * 8 + [ctypes.c_float, c_int, vp,
                                                                           ctypes.c_longlong, vp])
     lib.fa_fwd_splitkv.restype = c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = ([vp, vp, vp, vp, vp] + [c_int] * 8 + [ctypes.c_float, c_int, vp])
+    lib.fa_fwd_splitkv_noalloc.restype = c_int
     lib.fa_splitkv_splits.argtypes = [c_int] * 8
     lib.fa_splitkv_splits.restype = c_int
     lib.fa_splitkv_workspace_bytes.argtypes = [c_int] * 5
@@ -116,6 +122,15 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scal
                                         int(Hkv), int(D), int(bool(causal)), int(past_len),
                                         float(scale), int(n_splits), workspace,
                                         int(workspace_bytes), stream))
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale,
+                           n_splits, stream) -> int:
+    """Direct call of the allocation-free split-KV entry point (static device
+    scratch instead of a workspace); status returned unchanged."""
+    return int(library().fa_fwd_splitkv_noalloc(q, k, v, o, lse, int(B), int(Lq), int(Lk), int(H),
+                                                int(Hkv), int(D), int(bool(causal)), int(past_len),
+                                                float(scale), int(n_splits), stream))
 
 
 def fa_splitkv_splits(B, Lq, Lk, H, Hkv, D, causal, past_len) -> int:
@@ -238,6 +253,33 @@ def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None, o
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = fa_fwd_splitkv(*ptrs, B, L, Lk, H, Hkv, D, causal, past, scale, splits,
                             workspace.data_ptr() or None, ws_bytes, stream)
+    if st != 0:
+        raise FaError(st, fa_status_string(st))
+    return out, lse
+
+
+def forward_splitkv_noalloc(q, k, v, causal: bool = False, scale: float | None = None, out=None,
+                            lse=None, with_lse: bool = True, past_len: int | None = None,
+                            n_splits: int | None = None):
+    """forward_splitkv through fa_fwd_splitkv_noalloc: the library's static
+    device scratch holds the partial results, so the call itself allocates
+    nothing on the device (out and lse are allocated here only when not
+    given).  Calls that overlap on one GPU race on that scratch."""
+    import torch
+
+    _check_qkv(q, k, v)
+    B, L, H, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out, lse = _outputs(q, out, lse, with_lse)
+    past = Lk - L if past_len is None else int(past_len)
+    splits = 0 if n_splits is None else int(n_splits)
+    ptrs = (q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
+            out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd_splitkv_noalloc(*ptrs, B, L, Lk, H, Hkv, D, causal, past, scale, splits, stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return out, lse

@@ -198,6 +198,27 @@ extern "C" int fa_fwd_splitkv(const void *q, const void *k, const void *v, void 
     return fa::launch_splitkv(p, n_splits, workspace, stream);
 }
 
+extern "C" int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o,
+                                      float *lse, int B, int Lq, int Lk, int H, int Hkv, int D,
+                                      int causal, int past_len, float scale, int n_splits,
+                                      hipStream_t stream)
+{
+    fa::Problem p;
+    bool empty;
+    const int st = validate(q, k, v, o, lse, B, Lq, Lk, H, Hkv, D, causal, past_len, scale, &p, &empty);
+    if (st != FA_OK) return st;
+    if (n_splits < 0 || n_splits > kMaxSplits) return FA_ERR_SHAPE;
+    if (empty) return FA_OK;
+    if (n_splits == 0) n_splits = default_splits(B, Lq, Lk, H, Hkv, D, causal, past_len);
+    const int64_t need = fa::splitkv_workspace_bytes(elems4(B, H, Lq, 1), n_splits, D);
+    if (need < 0) return FA_ERR_SHAPE;
+    if (need > fa::kScratchBytes) return FA_ERR_SCRATCH;  // checked before any HIP call
+    void *scratch = nullptr;
+    const int sst = fa::splitkv_scratch(&scratch);
+    if (sst != FA_OK) return sst;
+    return fa::launch_splitkv(p, n_splits, scratch, stream);
+}
+
 extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
                       const void *dout, const float *lse, float *delta, void *dq, void *dk,
                       void *dv, int B, int L, int H, int Hkv, int D, int causal, float scale,
@@ -253,8 +274,12 @@ extern "C" const char *fa_status_string(int status)
     case FA_ERR_WORKSPACE:
         return "FA_ERR_WORKSPACE: workspace is NULL, smaller than fa_splitkv_workspace_bytes, "
                "or not 16-byte aligned";
+    case FA_ERR_SCRATCH:
+        return "FA_ERR_SCRATCH: fa_fwd_splitkv_noalloc needs more than its static scratch "
+               "(FA_SPLITKV_SCRATCH_BYTES = 16 MiB) holds; use fa_fwd_splitkv with a workspace "
+               "or fewer splits";
     default: return "FA_ERR_UNKNOWN";
     }
 }
 
-extern "C" int fa_abi_version(void) { return 5; }
+extern "C" int fa_abi_version(void) { return 6; }

@@ -39,6 +39,12 @@ int launch_forward_fp8(const Problem &p, Fp8Descale ds, hipStream_t stream);
 int64_t splitkv_workspace_bytes(int64_t rows_total, int64_t n_splits, int D);
 int launch_splitkv(const Problem &p, int n_splits, void *workspace, hipStream_t stream);
 
+// The static scratch of the allocation-free split-KV entry point: its size,
+// and its device address on the current device (looked up once per device).
+// Returns FA_OK or FA_ERR_DEVICE.
+constexpr int64_t kScratchBytes = FA_SPLITKV_SCRATCH_BYTES;
+int splitkv_scratch(void **ptr);
+
 // Validated backward problem (queries and keys equally long).
 struct BwdProblem {
     const void *q, *k, *v, *o, *dout;

@@ -37,6 +37,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -363,6 +366,37 @@ int launch_split(const SplitArgs &s, const MergeArgs &mg, hipStream_t stream)
 }
 
 }  // namespace
+
+// Scratch of fa_fwd_splitkv_noalloc: the partial results live in this
+// file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy for the life of the process.  In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is passed to kernels.
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+}  // namespace
+
+int splitkv_scratch(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return FA_ERR_DEVICE;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_DEVICE;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return FA_OK;
+}
 
 int64_t splitkv_workspace_bytes(int64_t rows_total, int64_t n_splits, int D)
 {
