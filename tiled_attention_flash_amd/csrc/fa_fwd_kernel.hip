@@ -77,6 +77,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <numeric>
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -93,7 +94,8 @@ struct Args {
     int Lq, Lk;    // query rows, key rows
     int past_len;  // position of query row 0 among the keys (causal mask only)
     int H, Hkv, groups, n_qblocks, n_items;
-    int n_units;  // causal (persistent grid): pairs of q blocks
+    int n_rows;      // causal (persistent grid): row groups, B * H
+    int phase_rows;  // causal: row groups per phase (see run())
     float scale;       // multiplier of Q.K
     float scale_log2;  // scale * log2(e): exp(scale*x) == exp2(scale_log2*x)
 };
@@ -507,14 +509,22 @@ struct Kernel : WaveMath<D, CAUSAL> {
     // Work decomposition.
     //  * Full pass: one workgroup per work item, xcd_item(blockIdx.x).
     //  * Causal (the loop of the pages' kernel over q blocks): persistent.  The
-    //    grid is the resident workgroups, a multiple of 8.  The units are
-    //    pairs of q blocks (nQ-1-i, i) of one row group, so that every unit
-    //    holds the same work (with past_len p and blocks of BM rows the pair
-    //    sees 2p + (nQ+1)BM keys in all).  They are cut into 8 contiguous
-    //    ranges, one per XCD (workgroups reach the XCDs round robin), and the
-    //    workgroups of an XCD take the units of its range in turn, the heavy
-    //    block of a pair first; a barrier separates consecutive items, whose
-    //    first loads reuse the LDS tiles.
+    //    grid is the resident workgroups, a multiple of 8, and the work items
+    //    are single q blocks, whose cost falls with the block index.  The row
+    //    groups are cut into 8 contiguous ranges, one per XCD (workgroups
+    //    reach the XCDs round robin), so that the query heads sharing a K/V
+    //    head stay in one L2.  An XCD walks its range in phases of C row
+    //    groups; a phase's items are ordered heaviest first (q block nQ-1 of
+    //    each of its row groups, then nQ-2, ...) and dealt to the XCD's gx
+    //    workgroups in rounds whose direction alternates, so the workgroup
+    //    that takes the heaviest item of one round takes the lightest of the
+    //    next.  C is the fewest row groups whose items fill an even number of
+    //    rounds (2 gx / gcd(nQ, 2 gx), from the host), which balances every
+    //    phase exactly while only C row groups' K/V are in use at a time;
+    //    where C does not divide the range, one phase covers it all (balanced
+    //    to within one item).  With fewer than 8 row groups the whole grid
+    //    deals all items the same way.  A barrier separates consecutive
+    //    items, whose first loads reuse the LDS tiles.
     __device__ static void run(const Args &a)
     {
         __shared__ __attribute__((aligned(16))) _Float16 klds[2][G::kTile];
@@ -526,22 +536,26 @@ struct Kernel : WaveMath<D, CAUSAL> {
             decode(a, it / nq, b, hk, h);
             item(a, b, hk, h, it % nq, klds, vlds);
         } else {
-            const int x = blockIdx.x % kXcds, per = a.n_units / kXcds, extra = a.n_units % kXcds;
-            const int first = x * per + (x < extra ? x : extra);
-            const int end = first + per + (x < extra ? 1 : 0);
-            const int stride = (int)gridDim.x / kXcds;
-            const int upg = (nq + 1) / 2;  // units (pairs) per row group
+            int gx = (int)gridDim.x, s = (int)blockIdx.x, rg0 = 0, nrg = a.n_rows;
+            if (a.n_rows >= kXcds) {
+                const int x = (int)blockIdx.x % kXcds, per = a.n_rows / kXcds, extra = a.n_rows % kXcds;
+                rg0 = x * per + (x < extra ? x : extra);
+                nrg = per + (x < extra ? 1 : 0);
+                gx /= kXcds;
+                s /= kXcds;
+            }
+            const int C = nrg % a.phase_rows == 0 ? a.phase_rows : nrg;
             bool started = false;
-            for (int u = first + (int)blockIdx.x / kXcds; u < end; u += stride) {
-                const int i = u % upg;
-                int b, hk, h;
-                decode(a, u / upg, b, hk, h);
-                for (int j = 0; j < 2; ++j) {
-                    const int qb = j == 0 ? nq - 1 - i : i;
-                    if (j == 1 && qb == nq - 1 - i) break;  // middle block of an odd count
+            for (int p0 = 0; p0 < nrg; p0 += C) {
+                const int n = C * nq;  // this phase's items
+                for (int r = 0;; ++r) {
+                    const int idx = r * gx + ((r & 1) ? gx - 1 - s : s);  // < items + grid < 2^31
+                    if (idx >= n) break;  // every later round starts past n as well
+                    int b, hk, h;
+                    decode(a, rg0 + p0 + idx % C, b, hk, h);
                     if (started) __syncthreads();  // every wavefront is done with the LDS tiles
                     started = true;
-                    item(a, b, hk, h, qb, klds, vlds);
+                    item(a, b, hk, h, nq - 1 - idx / C, klds, vlds);
                 }
             }
         }
@@ -598,19 +612,22 @@ int launch_w(Args args, hipStream_t stream)
     using K = Kernel<D, CAUSAL, W>;
     args.n_qblocks = (args.Lq + K::kBM - 1) / K::kBM;
     const int64_t items = (int64_t)args.n_items * args.n_qblocks;  // n_items holds B*H here
-    if (items > 0x7fffffff) return FA_ERR_SHAPE;
+    // the persistent schedule's item indices stay below items + grid; no
+    // problem that fits in memory comes near this bound
+    if (items > (1 << 30)) return FA_ERR_SHAPE;
     const int rows = args.n_items;
     args.n_items = (int)items;
     int grid = args.n_items;
-    args.n_units = 0;
+    args.n_rows = rows;
+    args.phase_rows = 1;
     if (K::kPersistent) {
         const int slots = resident_workgroups((const void *)fa_fwd_kernel<D, CAUSAL, W>, K::kThreads);
         if (slots <= 0) return FA_ERR_DEVICE;
-        const int64_t units = (int64_t)rows * ((args.n_qblocks + 1) / 2);
-        args.n_units = (int)units;  // <= items
         // a multiple of 8, so that blockIdx.x % 8 names the XCD for every slot
-        const int64_t want = units < slots ? units : slots;
+        const int64_t want = items < slots ? items : slots;
         grid = (int)((want + kXcds - 1) / kXcds * kXcds);
+        const int gx2 = 2 * (rows >= kXcds ? grid / kXcds : grid);
+        args.phase_rows = gx2 / std::gcd(args.n_qblocks, gx2);
     }
     if (grid == 0) return FA_OK;
     hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, W>), dim3(grid), dim3(K::kThreads), 0, stream, args);
