@@ -55,7 +55,9 @@ class Checker:
         self.nq = (Lq + self.BM - 1) // self.BM
         self.chunks = D // 8
         self.rpl = 64 // self.chunks           # rows one load instruction fills
-        self.lpw = (BN // self.rpl) // self.W  # load instructions per wave and tile
+        per_tile = BN // self.rpl              # load instructions per tile
+        self.loaders = min(self.W, per_tile)   # waves that load (the first ones)
+        self.lpw = per_tile // self.loaders    # load instructions per loading wave
         self.kv_row = Hkv * D                  # elements between key rows
         self.q_row = H * D
         self.kv_bytes = 2 * B * Lk * Hkv * D
@@ -69,7 +71,7 @@ class Checker:
     def lane_offsets(self, is_v):
         """init_load_offsets for every (wave, n) at once: rows [W*lpw, 64] and
         the lane offsets (uint32_t)(2 * (row * kv_row + 8 * chunk))."""
-        blk = np.arange(self.W * self.lpw)[:, None]  # blk = lpw * wave + n
+        blk = np.arange(self.loaders * self.lpw)[:, None]  # blk = lpw * wave + n
         row = self.rpl * blk + self.lane[None, :] // self.chunks
         pc = np.broadcast_to(self.lane[None, :] % self.chunks, row.shape)
         ch = v_chunk(self.D, row, pc) if is_v else k_chunk(self.D, row, pc)

@@ -144,24 +144,24 @@ __device__ __forceinline__ void init_load_offsets(LoadOffsets<D, W> &lo, int64_t
 }
 
 // Issue this wave's share of the direct loads of the K (or V) tile that
-// starts at key k0.  A tile reaching past Lk loads row Lk-1 in place of the
-// missing rows (finite data that the mask hides); rows before key 0 (the
-// first K tile starts at key -32) are not loaded and never read.
-template <int D, int W, bool IS_V>
-__device__ __forceinline__ void issue_loads(const LoadOffsets<D, W> &lo, const _Float16 *base,
-                                            int64_t kv_row, int k0, int Lk, _Float16 *lds, int tid)
+// starts at key k0, whose key row 0 is at `tile` (k0 * kv_row elements past
+// the head's key 0).  EDGE: the tile may start before key 0 or reach past
+// Lk.  Then a row past the end re-reads row Lk-1 (finite data that the mask
+// hides), and an instruction whose rows all lie before key 0 (the first K
+// tile starts at key -32) is not issued -- those rows are never read.  A
+// tile with every row inside [0, Lk) takes the lane offsets as they are.
+template <int D, int W, bool IS_V, bool EDGE>
+__device__ __forceinline__ void issue_loads(const LoadOffsets<D, W> &lo, const char *tile, int64_t kv_row,
+                                            int k0, int Lk, _Float16 *lds, int wave, int tid)
 {
     using G = Geo<D, W>;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const char *tile = (const char *)(base + (int64_t)k0 * kv_row);
-    const bool full = k0 + kBN <= Lk;
 #pragma unroll
     for (int n = 0; n < G::kLoadsPerWave; ++n) {
         const int blk = G::kLoadsPerWave * wave + n;
-        if (k0 + G::kRowsPerLoad * blk < 0) continue;  // whole instruction before key 0
         uint32_t off = IS_V ? lo.v[n] : lo.k[n];
-        if (!full) {
-            const int over = k0 + load_row<D, W>(tid, n) - (Lk - 1);  // rows past the end re-read row Lk-1
+        if constexpr (EDGE) {
+            if (k0 + G::kRowsPerLoad * blk < 0) continue;  // whole instruction before key 0
+            const int over = k0 + load_row<D, W>(tid, n) - (Lk - 1);
             if (over > 0) off -= (uint32_t)(2 * over * kv_row);
         }
         dma16(tile, off, lds + 512 * blk);
@@ -276,11 +276,12 @@ struct Kernel : WaveMath<D, CAUSAL> {
     // V(t-1), whose buffers then receive K(t+1) and V(t+1).
     struct Ring {
         const LoadOffsets<D, W> *lo;
-        const _Float16 *kbase, *vbase;
+        const char *k0tile, *v0tile;  // K tile 0 (keys 32..95), V tile 0 (keys 0..63)
+        uint32_t tile_stride;         // bytes between consecutive tiles' first key rows
         int64_t kv_row;
         int n_tiles, n_blocks, Lk, qp;
         int h4;  // 4 * (lane / 32): key offset of the lane's half in a score block
-        int tid;
+        int tid, wave;
         float c;
         _Float16 (*klds)[G::kTile];
         _Float16 (*vlds)[G::kTile];
@@ -297,10 +298,21 @@ struct Kernel : WaveMath<D, CAUSAL> {
     __device__ __forceinline__ static void tile_start(const Ring &r, int t)
     {
         tile_wait();
-        if (2 * t + 3 < r.n_blocks)
-            issue_loads<D, W, false>(*r.lo, r.kbase, r.kv_row, kBN * (t + 1) + kSB, r.Lk, r.klds[P], r.tid);
-        if (t + 1 < r.n_tiles)
-            issue_loads<D, W, true>(*r.lo, r.vbase, r.kv_row, kBN * (t + 1), r.Lk, r.vlds[P ^ 1], r.tid);
+        const int64_t step = (int64_t)(t + 1) * r.tile_stride;
+        if (2 * t + 3 < r.n_blocks) {
+            const int k0 = kBN * (t + 1) + kSB;
+            if (k0 + kBN <= r.Lk)
+                issue_loads<D, W, false, false>(*r.lo, r.k0tile + step, r.kv_row, k0, r.Lk, r.klds[P], r.wave, r.tid);
+            else
+                issue_loads<D, W, false, true>(*r.lo, r.k0tile + step, r.kv_row, k0, r.Lk, r.klds[P], r.wave, r.tid);
+        }
+        if (t + 1 < r.n_tiles) {
+            const int v0 = kBN * (t + 1);
+            if (v0 + kBN <= r.Lk)
+                issue_loads<D, W, true, false>(*r.lo, r.v0tile + step, r.kv_row, v0, r.Lk, r.vlds[P ^ 1], r.wave, r.tid);
+            else
+                issue_loads<D, W, true, true>(*r.lo, r.v0tile + step, r.kv_row, v0, r.Lk, r.vlds[P ^ 1], r.wave, r.tid);
+        }
     }
 
     // a tile whose two blocks both have a successor; MASK: mask both blocks
@@ -406,8 +418,11 @@ struct Kernel : WaveMath<D, CAUSAL> {
             // while Q is fetched
             LoadOffsets<D, W> lo;
             init_load_offsets<D, W>(lo, kv_row, tid);
-            issue_loads<D, W, false>(lo, kbase, kv_row, -kSB, Lk, klds[0], tid);
-            issue_loads<D, W, true>(lo, vbase, kv_row, 0, Lk, vlds[0], tid);
+            const char *k0tile = (const char *)(kbase + kSB * kv_row);
+            const char *v0tile = (const char *)vbase;
+            const uint32_t tile_stride = (uint32_t)(2 * kBN * kv_row);  // < 2^31 (the host checks Hkv*D)
+            issue_loads<D, W, false, true>(lo, k0tile - tile_stride, kv_row, -kSB, Lk, klds[0], wave, tid);
+            issue_loads<D, W, true, true>(lo, v0tile, kv_row, 0, Lk, vlds[0], wave, tid);
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
                 half8 val = {};
@@ -420,11 +435,12 @@ struct Kernel : WaveMath<D, CAUSAL> {
 
             // prologue: scores and exact reference maximum of block 0; K tile 0 in flight
             const int wlast = __builtin_amdgcn_readfirstlane(wq0 + 31 + a.past_len);
-            const Ring r{&lo, kbase, vbase, kv_row, n_tiles, n_blocks, Lk, qp, 4 * half, tid, c, klds, vlds, wlast};
+            const Ring r{&lo, k0tile, v0tile, tile_stride, kv_row, n_tiles, n_blocks, Lk, qp, 4 * half, tid, wave, c,
+                         klds, vlds, wlast};
             floatx16 sa, sb;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (n_blocks > 1) issue_loads<D, W, false>(lo, kbase, kv_row, kSB, Lk, klds[1], tid);
+            if (n_blocks > 1) issue_loads<D, W, false, true>(lo, k0tile, kv_row, kSB, Lk, klds[1], wave, tid);
             s_product(sa, st, klds[0] + kSB * D);
             mask(sa, 0, Lk, qp, 4 * half);
             rescale(st, block_max(sa), c);
