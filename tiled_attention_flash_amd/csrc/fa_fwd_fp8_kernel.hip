@@ -101,29 +101,39 @@ __device__ __forceinline__ int load_row8(int wave, int n)
     return G::kRowsPerLoad * (wave + W * n) + (threadIdx.x & 63) / G::kChunks;
 }
 
-// Issue this wave's share of the direct loads of the tile at key k0 (rows
-// past the end re-read row Lk - 1: finite data that the mask hides).
-// offs[n]: byte offset of this lane's chunk of load n relative to the tile.
-template <int D, int W>
+// Issue this wave's share of the direct loads of the tile at key k0, whose
+// key row 0 is at `tile`.  EDGE: the tile may reach past Lk; rows past the
+// end re-read row Lk - 1 (finite data that the mask hides).  offs[n]: byte
+// offset of this lane's chunk of load n relative to the tile.
+template <int D, int W, bool EDGE>
 __device__ __forceinline__ void issue_tile8(const uint32_t (&offs)[Geo8<D, W>::kLoadsPerWave],
-                                            const uint8_t *base, int64_t kv_row, int k0, int Lk,
-                                            uint8_t *lds)
+                                            const char *tile, int64_t kv_row, int k0, int Lk, uint8_t *lds)
 {
     using G = Geo8<D, W>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const char *tile = (const char *)(base + (int64_t)k0 * kv_row);
-    const bool full = k0 + kBlk <= Lk;
 #pragma unroll
     for (int n = 0; n < G::kLoadsPerWave; ++n) {
         const int blk = wave + W * n;
         if (G::kLoadsPerTile % W != 0 && blk >= G::kLoadsPerTile) continue;  // wave-uniform
         uint32_t off = offs[n];
-        if (!full) {
+        if constexpr (EDGE) {
             const int over = k0 + load_row8<D, W>(wave, n) - (Lk - 1);
             if (over > 0) off -= (uint32_t)(over * kv_row);
         }
         dma16(tile, off, (_Float16 *)(lds + 1024 * blk));
     }
+}
+
+// The tile at key k0 = kBlk * j: its first row lies j * kBlk * kv_row bytes
+// past the head's key 0 (kBlk * kv_row < 2^31, checked on the host).
+template <int D, int W>
+__device__ __forceinline__ void issue_tile8_at(const uint32_t (&offs)[Geo8<D, W>::kLoadsPerWave],
+                                               const uint8_t *base, int64_t kv_row, int j, int Lk, uint8_t *lds)
+{
+    const char *tile = (const char *)base + (int64_t)j * (uint32_t)(kBlk * kv_row);
+    const int k0 = kBlk * j;
+    if (k0 + kBlk <= Lk) issue_tile8<D, W, false>(offs, tile, kv_row, k0, Lk, lds);
+    else issue_tile8<D, W, true>(offs, tile, kv_row, k0, Lk, lds);
 }
 
 template <int D, bool CAUSAL, int W>
@@ -352,8 +362,8 @@ struct Kernel8 {
     {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (u + 2 < n_blocks) issue_tile8<D, W>(offs, kbase, kv_row, kBlk * (u + 2), Lk, klds[P]);
-        if (u + 1 < n_blocks) issue_tile8<D, W>(offs, vbase, kv_row, kBlk * (u + 1), Lk, vlds[P ^ 1]);
+        if (u + 2 < n_blocks) issue_tile8_at<D, W>(offs, kbase, kv_row, u + 2, Lk, klds[P]);
+        if (u + 1 < n_blocks) issue_tile8_at<D, W>(offs, vbase, kv_row, u + 1, Lk, vlds[P ^ 1]);
         step<NEXT, MASK>(st, sc, sn, klds[P ^ 1], vlds[P], kBlk * u, Lk, qp, c);
     }
 
@@ -405,8 +415,8 @@ struct Kernel8 {
                     offs[n] = (uint32_t)(row * kv_row + 16 * (pc ^ f8_swz<D>(row)));
                 }
             }
-            issue_tile8<D, W>(offs, kbase, kv_row, 0, Lk, klds[0]);
-            issue_tile8<D, W>(offs, vbase, kv_row, 0, Lk, vlds[0]);
+            issue_tile8_at<D, W>(offs, kbase, kv_row, 0, Lk, klds[0]);
+            issue_tile8_at<D, W>(offs, vbase, kv_row, 0, Lk, vlds[0]);
 #pragma unroll
             for (int s = 0; s < kS; ++s) {
                 int8v val = {};
@@ -424,7 +434,7 @@ struct Kernel8 {
             floatx16 sa[2], sb[2];
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (n_blocks > 1) issue_tile8<D, W>(offs, kbase, kv_row, kBlk, Lk, klds[1]);
+            if (n_blocks > 1) issue_tile8_at<D, W>(offs, kbase, kv_row, 1, Lk, klds[1]);
             s_product(sa, st, klds[0]);
             mask(sa, 0, Lk, qp);
             raise_to(st, block_max(sa), c);
