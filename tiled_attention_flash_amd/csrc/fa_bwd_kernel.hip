@@ -137,6 +137,27 @@ struct TileLoad {
     }
 };
 
+// One 4-byte-per-lane direct HBM -> LDS load: the dword at base + off of
+// lane i lands at lds + 4*i (lanes outside the exec mask write nothing).
+// Like dma16, inline assembly, so the compiler does not wait for it before
+// later LDS reads; the kernel waits for its loads itself.  `base` must be
+// the same in every lane; it passes through readfirstlane so that it is
+// held in scalar registers (the instruction's base operand) even where the
+// compiler would otherwise keep the computed address in vector registers.
+// A vector instruction that writes a scalar register (readfirstlane does)
+// must be 5 wait states ahead of a memory instruction that reads it, and
+// the compiler does not count the load inside the assembly: the s_nop 4
+// supplies them (and the one wait state an M0 write needs before the load).
+__device__ __forceinline__ void dma4(const char *base, uint32_t off, void *lds)
+{
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const char *sbase = (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    const uint32_t m0 = (uint32_t)(uintptr_t)(LDS_AS void *)lds;
+    __asm__ volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
 struct BwdArgs {
     const _Float16 *q, *k, *v, *o, *dout;
     const float *lse;
@@ -209,13 +230,58 @@ struct DkDv {
         const _Float16 *gb = a.dout + (int64_t)b * a.L * row_stride + (int64_t)h * D;
         Load::issue(qb, row_stride, q0, a.L, sm.q[P]);
         Load::issue(gb, row_stride, q0, a.L, sm.g[P]);
-        // LSE and Delta of the 32 rows; rows past the end get LSE = +inf
-        // (probability 0) and Delta = 0
+        // LSE and Delta of the 32 rows, by direct loads of lanes 0..31 of
+        // wave 0 (a load into VGPRs and an LDS store would wait for the
+        // tile loads just issued).  Rows past the end re-read row L-1; on
+        // the one block per head that has such rows, wave 0 waits for its
+        // loads and sets their LSE to +inf (probability 0), before the
+        // barrier that precedes any read of the block.
         if (threadIdx.x < kBQ) {
-            const int i = q0 + (int)threadIdx.x;
-            const int64_t r = ((int64_t)b * a.H + h) * a.L + i;
-            sm.lse[P][threadIdx.x] = i < a.L ? a.lse[r] : __builtin_huge_valf();
-            sm.delta[P][threadIdx.x] = i < a.L ? a.delta[r] : 0.0f;
+            const int i = q0 + (int)threadIdx.x < a.L ? q0 + (int)threadIdx.x : a.L - 1;
+            const int64_t r0 = ((int64_t)b * a.H + h) * a.L;  // row 0 of (b, h); 4 i < 2^32
+            dma4((const char *)(a.lse + r0), (uint32_t)(4 * i), sm.lse[P]);
+            dma4((const char *)(a.delta + r0), (uint32_t)(4 * i), sm.delta[P]);
+            if (q0 + kBQ > a.L) {
+                __builtin_amdgcn_s_waitcnt(0);
+                if (q0 + (int)threadIdx.x >= a.L) sm.lse[P][threadIdx.x] = __builtin_huge_valf();
+            }
+        }
+    }
+
+    // P and dS of one 32 x 32 block as fp16 B operands: P = exp2(c s -
+    // log2(e) LSE) for the visible (query, key) pairs, 0 elsewhere (rows
+    // past the last query have LSE = +inf), and dS = P (dP - Delta).
+    __device__ __forceinline__ static void probs(const floatx16 &s, const floatx16 &dp, const float *lse,
+                                                 const float *delta, int q0, int key, int L, int half, float c,
+                                                 half8 (&pf)[2], half8 (&sf)[2])
+    {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const float4v l4 = *(const float4v *)(&lse[8 * I + 4 * half]);
+            const float4v d4 = *(const float4v *)(&delta[8 * I + 4 * half]);
+            float pv[4], dsv[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const int r = 4 * I + J;
+                const int qi = q0 + 8 * I + 4 * half + J;
+                float p = exp2_fast(__builtin_fmaf(s[r], c, -kLog2e * l4[J]));
+                if ((CAUSAL && key > qi) || key >= L) p = 0.0f;
+                pv[J] = p;
+                dsv[J] = p * (dp[r] - d4[J]);
+            }
+            // register r -> k-step r/8, position r%8
+#pragma unroll
+            for (int J = 0; J < 4; J += 2) {
+                const int r = 4 * I + J;
+                const float2v p2 = {pv[J], pv[J + 1]};
+                const float2v d2 = {dsv[J], dsv[J + 1]};
+                const half2v hp = __builtin_convertvector(p2, half2v);
+                const half2v hd = __builtin_convertvector(d2, half2v);
+                pf[r >> 3][r & 7] = hp[0];
+                pf[r >> 3][(r & 7) + 1] = hp[1];
+                sf[r >> 3][r & 7] = hd[0];
+                sf[r >> 3][(r & 7) + 1] = hd[1];
+            }
         }
     }
 
@@ -289,36 +355,8 @@ struct DkDv {
                     s = __builtin_amdgcn_mfma_f32_32x32x16_f16(tr.row_frag(qt, st), kf[st], s, 0, 0, 0);
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(tr.row_frag(gt, st), tr.row_frag(vt, st), dp, 0, 0, 0);
                 }
-                // P = exp2(c s - log2(e) LSE), masked; dS = P (dP - Delta)
                 half8 pf[2], sf[2];
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    const float4v l4 = *(const float4v *)(&sm.lse[P][8 * I + 4 * half]);
-                    const float4v d4 = *(const float4v *)(&sm.delta[P][8 * I + 4 * half]);
-                    float pv[4], dsv[4];
-#pragma unroll
-                    for (int J = 0; J < 4; ++J) {
-                        const int r = 4 * I + J;
-                        const int qi = q0 + 8 * I + 4 * half + J;
-                        float p = exp2_fast(__builtin_fmaf(s[r], c, -kLog2e * l4[J]));
-                        if ((CAUSAL && key > qi) || key >= L) p = 0.0f;
-                        pv[J] = p;
-                        dsv[J] = p * (dp[r] - d4[J]);
-                    }
-                    // register r -> k-step r/8, position r%8
-#pragma unroll
-                    for (int J = 0; J < 4; J += 2) {
-                        const int r = 4 * I + J;
-                        const float2v p2 = {pv[J], pv[J + 1]};
-                        const float2v d2 = {dsv[J], dsv[J + 1]};
-                        const half2v hp = __builtin_convertvector(p2, half2v);
-                        const half2v hd = __builtin_convertvector(d2, half2v);
-                        pf[r >> 3][r & 7] = hp[0];
-                        pf[r >> 3][(r & 7) + 1] = hp[1];
-                        sf[r >> 3][r & 7] = hd[0];
-                        sf[r >> 3][(r & 7) + 1] = hd[1];
-                    }
-                }
+                probs(s, dp, sm.lse[P], sm.delta[P], q0, key, L, half, c, pf, sf);
                 // dV^T += dO^T.P, dK^T += Q^T.dS (A operands transposed)
 #pragma unroll
                 for (int cs = 0; cs < 2; ++cs)
