@@ -41,7 +41,9 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_NULLPTR = 1,  /* q, k, v or o is NULL                                  */
     FA_ERR_SHAPE = 2,    /* a size is negative or overflows int64; fa_fwd_kv also:
-                            Lq or Lk > 2^30, or |past_len| > 2^30              */
+                            Lq or Lk > 2^30, or |past_len| > 2^30; the forward
+                            entry points: 64 rows of K span 2 GiB or more;
+                            fa_bwd: 256 rows of Q do (H*D >= 2^22)          */
     FA_ERR_GQA = 3,      /* Hkv <= 0, H <= 0, or H not a multiple of Hkv           */
     FA_ERR_HEADDIM = 4,  /* D is not 64 or 128                                     */
     FA_ERR_SCALE = 5,    /* scale is not finite or not > 0                         */

@@ -334,6 +334,8 @@ def call_bwd(**kw):
     (dict(scale=0.0), 5), (dict(dout=DO + 8), 6), (dict(delta=DELTA + 2), 6), (dict(dk=DK + 4), 6),
     (dict(dq=Q), 7), (dict(dk=DV), 7), (dict(delta=LSE), 7), (dict(dv=O + 64), 7),
     (dict(dq=DO - 1024), 7), (dict(delta=DQ + 256), 7),
+    # 256 rows of a 32768-head, D = 128 tensor span 2 GiB: tile offsets would not fit 32 bits
+    (dict(H=32768, Hkv=32768, D=128, L=1), 2),
 ])
 def test_bwd_invalid_arguments_rejected_without_launch(kw, status):
     assert call_bwd(**kw) == status

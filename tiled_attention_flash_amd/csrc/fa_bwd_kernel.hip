@@ -574,8 +574,9 @@ int launch_bwd(BwdArgs a, int B, hipStream_t stream)
 
 int launch_backward(const BwdProblem &p, hipStream_t stream)
 {
-    // per-lane tile offsets are 32-bit: 64 rows of the widest tensor must span < 2 GiB
-    if ((int64_t)p.H * p.D * 2 * 64 > 0x7fffffff) return FA_ERR_SHAPE;
+    // per-lane tile offsets are 32-bit: the tallest staged tile, 256 rows
+    // (the dK/dV kernel's V rows), of the widest tensor must span < 2 GiB
+    if ((int64_t)p.H * p.D * 2 * 256 > 0x7fffffff) return FA_ERR_SHAPE;
     BwdArgs a;
     a.q = (const _Float16 *)p.q;
     a.k = (const _Float16 *)p.k;
