@@ -6,7 +6,8 @@ single q blocks of one (batch, query head) row group -- to them: the row
 groups are cut into 8 contiguous ranges, one per XCD; an XCD walks its range
 in phases of C row groups, and a phase's items, ordered heaviest first
 (block nQ-1 of each of its row groups, then nQ-2, ...), are dealt in rounds
-whose direction alternates.  This model repeats that index arithmetic and
+whose direction alternates (with several phases, to a permuted slot order
+that gives a row group consecutive slots).  This model repeats that index arithmetic and
 checks that every item is dealt exactly once, that every workgroup is on
 the XCD of its row groups, that a phase holds few row groups, and that the
 work per workgroup is balanced on the benchmark shapes.
@@ -46,6 +47,9 @@ def schedule(rows, nq, grid):
             gx //= XCDS
             s //= XCDS
         c = c0 if nrg % c0 == 0 else nrg
+        if c < nrg and gx % c == 0:  # several phases: a row group's slots made consecutive
+            m = gx // c
+            s = (s % m) * c + s // m
         mine = []
         for p0 in range(0, nrg, c):
             n = c * nq

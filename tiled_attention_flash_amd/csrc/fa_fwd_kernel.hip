@@ -561,6 +561,15 @@ struct Kernel : WaveMath<D, CAUSAL> {
                 s /= kXcds;
             }
             const int C = nrg % a.phase_rows == 0 ? a.phase_rows : nrg;
+            // With several phases, the slots that take one row group's items
+            // in a round are made consecutive (slot s deals as s'), which
+            // spreads a row group over the XCD's compute units (measured:
+            // HBM reads of the causal B=8 H=32 L=4096 pass -31 %, 2 % faster;
+            // a single phase keeps the plain order, 5 % faster at D = 64)
+            if (C < nrg && gx % C == 0) {
+                const int m = gx / C;
+                s = (s % m) * C + s / m;
+            }
             bool started = false;
             for (int p0 = 0; p0 < nrg; p0 += C) {
                 const int n = C * nq;  // this phase's items
