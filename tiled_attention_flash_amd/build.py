@@ -1,7 +1,8 @@
 """Builds libfa.so (the C-ABI attention library) for gfx950 with hipcc, in-tree.
 
 Usage: ``python -m tiled_attention_flash_amd.build``.  Compiles every time it
-is called.
+is called, then checks the kernels' assembly (isa_check) and fails if a
+direct load could read a wrong base address.
 """
 from __future__ import annotations
 
@@ -51,9 +52,22 @@ def build_shared(sources, out, include_dirs=(), extra=()) -> str:
     return out
 
 
+def check_assembly() -> None:
+    """Build the kernel sources to assembly and refuse code whose direct
+    loads could read a wrong base address (see isa_check)."""
+    import tempfile
+    from . import isa_check
+    with tempfile.TemporaryDirectory() as tmp:
+        bad = isa_check.problems(isa_check.assemble_all(tmp))
+    if bad:
+        raise RuntimeError("kernel assembly check failed:\n" + "\n".join(bad[:20]))
+
+
 def build() -> str:
     build_shared([os.path.join(CSRC, "fa_clock_probe.hip")], CLOCK_LIB)
-    return build_shared([os.path.join(CSRC, s) for s in SOURCES], LIB, include_dirs=[INCLUDE, CSRC])
+    lib = build_shared([os.path.join(CSRC, s) for s in SOURCES], LIB, include_dirs=[INCLUDE, CSRC])
+    check_assembly()
+    return lib
 
 
 if __name__ == "__main__":
