@@ -374,3 +374,55 @@ def test_reference_maximum_overruns(pattern, causal, D):
     o_ref, lse_ref = oracle.forward(q, k, v, causal=causal)
     o, lse = gpu_forward(q, k, v, causal)
     assert_close(o, lse, o_ref, lse_ref, f"overrun {pattern} D={D} causal={causal}")
+
+
+# ------------------------------------------------- causal persistent schedule
+#
+# Under the causal mask the kernel runs a persistent grid (one workgroup per
+# resident slot) that deals single q blocks in rounds, per XCD and in phases
+# of a few row groups (see fa_fwd_kernel.hip; tests/test_schedule.py models
+# the index arithmetic).  The shapes below make workgroups take several items
+# and reach the schedule's paths at sizes the oracle checks in seconds:
+# uneven per-XCD ranges of row groups, an odd number of q blocks, queries
+# after cached keys, and several phases (where the slot order is permuted).
+SCHEDULE_CASES = [
+    # B, Lq, Lk, H, Hkv, D: what it reaches
+    (4, 1000, 1000, 25, 5, 64),     # 100 row groups (12 or 13 per XCD), 800 items on 768 slots
+    (3, 1100, 1100, 25, 5, 128),    # 75 row groups, 9 q blocks (odd), 675 items on 512 slots
+    (2, 900, 2000, 36, 12, 128),    # 1100 cached keys, 576 items on 512 slots
+]
+
+
+@pytest.mark.parametrize("case", SCHEDULE_CASES, ids=[f"b{c[0]}-q{c[1]}-k{c[2]}-h{c[3]}-kv{c[4]}-d{c[5]}"
+                                                      for c in SCHEDULE_CASES])
+def test_causal_schedule_whole_outputs(case):
+    B, Lq, Lk, H, Hkv, D = case
+    q, k, v = make_qkv(B, Lq, H, Hkv, D, seed=700 + Lq + H, Lk=Lk)
+    o_ref, lse_ref = oracle.forward(q, k, v, causal=True, past_len=Lk - Lq)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=True, past_len=Lk - Lq)
+    torch.cuda.synchronize()
+    assert_close(o.cpu(), lse.cpu(), o_ref, lse_ref, f"causal schedule B{B} Lq{Lq} Lk{Lk} H{H} Hkv{Hkv} D{D}")
+
+
+def test_causal_schedule_several_phases():
+    """B=4, H=32 (Hkv=8), L=2048, D=128: 128 row groups, 16 per XCD, in two
+    phases of 8 with the permuted slot order; 2048 items on 512 slots.  Whole
+    (b, h) slices at the corners and of one GQA group, and sampled rows over
+    every head."""
+    B, L, H, Hkv, D = 4, 2048, 32, 8, 128
+    q, k, v = make_qkv(B, L, H, Hkv, D, seed=777)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    oc, lc = o.cpu(), lse.cpu()
+    g = H // Hkv
+    for b, h in [(0, 0), (0, 1), (0, 2), (0, 3), (3, 31), (2, 17)]:
+        hk = h // g
+        o_ref, lse_ref = oracle.forward(q[b:b + 1, :, h:h + 1].contiguous(), k[b:b + 1, :, hk:hk + 1].contiguous(),
+                                        v[b:b + 1, :, hk:hk + 1].contiguous(), causal=True)
+        assert_close(oc[b:b + 1, :, h:h + 1], lc[b:b + 1, h:h + 1], o_ref, lse_ref, f"several phases slice b{b} h{h}")
+    rng = np.random.default_rng(5)
+    ids = np.array([(int(rng.integers(B)), h, int(rng.integers(L))) for h in range(H) for _ in range(6)])
+    o_ref, lse_ref = oracle.rows(q, k, v, ids, causal=True)
+    o_got = torch.stack([oc[b, i, h] for b, h, i in ids])
+    l_got = torch.stack([lc[b, h, i] for b, h, i in ids])
+    assert_close(o_got, l_got, o_ref, lse_ref, f"several phases, {len(ids)} sampled rows")
