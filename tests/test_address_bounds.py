@@ -21,7 +21,7 @@ would not:
   being the destination of the load instruction.
 
 Instances are chosen as the launcher chooses them: D = 128 full pass with 8
-wavefronts, causal with 4 below 8192 keys and 8 from 8192 on; D = 64 with 4.
+wavefronts, causal with 4 below 4096 keys and 8 from 4096 on; D = 64 with 4.
 """
 from __future__ import annotations
 
@@ -34,7 +34,7 @@ U32 = np.uint64(1 << 32)
 
 def waves_for(D, causal, Lk):
     if D == 128 and causal:
-        return 8 if Lk >= 8192 else 4
+        return 8 if Lk >= 4096 else 4
     return 4 if D == 64 else 8
 
 
@@ -212,9 +212,9 @@ def test_queries_after_cached_keys_in_bounds(case, causal):
         assert Checker(B, Lq, Lk, H, Hkv, D, causal, past).run() > 0
 
 
-@pytest.mark.parametrize("Lk", [8191, 8192, 8193, 8257])
+@pytest.mark.parametrize("Lk", [4095, 4096, 4097, 4161, 8193, 8257])
 def test_eight_wavefront_causal_in_bounds(Lk):
-    """Causal over 8192 keys or more selects the 8-wavefront D = 128 instance."""
+    """Causal over 4096 keys or more selects the 8-wavefront D = 128 instance."""
     assert Checker(1, Lk, Lk, 2, 1, 128, True, 0).run() > 0
     assert Checker(1, 300, Lk, 2, 2, 128, True, Lk - 300).run() > 0
 

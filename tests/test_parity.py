@@ -310,10 +310,12 @@ def test_query_and_key_lengths_differ(case, causal):
         assert d.max() <= MAX_O and d.mean() <= MEAN_O and dl.max() <= MAX_LSE, msg
 
 
-# Under the causal mask, 8192 keys or more select the eight-wavefront (256-row)
+# Under the causal mask, 4096 keys or more select the eight-wavefront (256-row)
 # forward instance; these cases cover its ragged ends, grouped heads and a
 # cached prefix, every row against the oracle.
 LONG_CAUSAL_CASES = [
+    (1, 4097, 4097, 2, 1, 128, None),   # one key past the switch, ragged everywhere
+    (1, 1000, 4100, 2, 2, 128, None),   # 1000 queries after 3100 cached keys
     (1, 8257, 8257, 2, 1, 128, None),   # ragged against 256-row blocks and 64-key tiles
     (1, 300, 8300, 2, 2, 128, None),    # queries after 8000 cached keys
     (1, 8192, 8192, 4, 1, 128, None),   # four query heads per K/V head
@@ -327,7 +329,7 @@ def test_long_causal_ragged(case):
 
 
 def test_long_causal_wide_logits(record_property):
-    """The eight-wavefront causal instance (8192 keys or more) on Q, K x 3,
+    """The eight-wavefront causal instance (4096 keys or more) on Q, K x 3,
     where rows take the reference-maximum fixup, every element against the
     oracle: L = 8192 + 75 (ragged), two query heads on one K/V head."""
     q, k, v = make_qkv(1, 8267, 2, 1, 128, seed=71, qk_mult=3.0)

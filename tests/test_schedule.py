@@ -95,7 +95,7 @@ def test_heaviest_first_within_a_workgroup():
         assert items and items[0][1] == max(qb for _, qb in items)
 
 
-@pytest.mark.parametrize("rows,nq,slots,c", [(256, 32, 512, 4), (64, 32, 256, 2), (32, 64, 256, 1),
+@pytest.mark.parametrize("rows,nq,slots,c", [(256, 32, 512, 4), (256, 16, 256, 4), (64, 32, 256, 2), (32, 64, 256, 1),
                                              (256, 8, 512, 16)])
 def test_phases_hold_few_row_groups(rows, nq, slots, c):
     """Where a phase divides an XCD's range, the workgroups of an XCD work
@@ -114,10 +114,11 @@ def test_phases_hold_few_row_groups(rows, nq, slots, c):
 # Benchmark shapes: (rows = B*H, Lq, Lk, q rows per workgroup, resident slots)
 SHAPES = {
     "B=8 H=32 L=1024 D=64 causal (W=4, 3 workgroups/CU)": (256, 1024, 1024, 128, 768),
-    "B=8 H=32 L=4096 D=128 causal (W=4, 2 workgroups/CU)": (256, 4096, 4096, 128, 512),
+    "B=8 H=32 L=4096 D=128 causal (W=8)": (256, 4096, 4096, 256, 256),
+    "B=8 H=32 L=2048 D=128 causal (W=4, 2 workgroups/CU)": (256, 2048, 2048, 128, 512),
     "GQA B=2 H=32 L=8192 D=128 causal (W=8)": (64, 8192, 8192, 256, 256),
     "B=1 H=32 L=16384 D=128 causal (W=8)": (32, 16384, 16384, 256, 256),
-    "prefill B=8 H=32 1024 queries after 3072 keys (W=4)": (256, 1024, 4096, 128, 512),
+    "prefill B=8 H=32 1024 queries after 3072 keys (W=8)": (256, 1024, 4096, 256, 256),
 }
 
 

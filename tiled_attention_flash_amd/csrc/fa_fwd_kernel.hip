@@ -16,7 +16,7 @@
 //   the full (non-causal) pass at D = 128 -- each K/V tile brought into LDS
 //   then serves 256 queries -- and W = 4 under the causal mask, where the
 //   smaller block keeps the wavefronts of a workgroup evenly loaded along the
-//   diagonal (W = 8 again from 8192 keys on, where the diagonal is a small
+//   diagonal (W = 8 again from 4096 keys on, where the diagonal is a small
 //   share of each work item), and at D = 64, where the shorter tiles favour
 //   independent workgroups: three per CU (three wavefronts per SIMD).
 // * Both products are computed transposed, on v_mfma_f32_32x32x16_f16:
@@ -662,14 +662,16 @@ int launch_w(Args args, hipStream_t stream)
 // Wavefronts per workgroup, measured per workload (same-process A/B): 8 for
 // the full pass at D = 128 (each K/V tile serves 256 queries); 4 at D = 64
 // and under the causal mask, where a 256-row block leaves half its
-// wavefronts computing masked blocks along the diagonal -- except for long
-// causal sequences (8192 keys or more), where the diagonal is a small share
-// of a work item and halving the K/V tile traffic per flop wins.
+// wavefronts computing masked blocks along the diagonal -- except from 4096
+// keys on, where the diagonal is a small share of a work item and halving
+// the K/V tile traffic per flop wins (measured: W = 4 is 4-25 % faster at
+// 512-2048 keys, W = 8 about 1 % at 4096 and 3 % for 1024 queries after
+// 3072 cached keys).
 template <int D, bool CAUSAL>
 int launch(Args args, hipStream_t stream)
 {
     if constexpr (D == 128 && CAUSAL) {
-        if (args.Lk >= 8192) return launch_w<D, CAUSAL, 8>(args, stream);
+        if (args.Lk >= 4096) return launch_w<D, CAUSAL, 8>(args, stream);
         return launch_w<D, CAUSAL, 4>(args, stream);
     } else {
         return launch_w<D, CAUSAL, (D == 64 ? 4 : 8)>(args, stream);
