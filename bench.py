@@ -197,10 +197,16 @@ def cpu_baseline(w, q, k, v, target_s: float, descale=None):
                             "(the host share of one GPU on a shared box)"}
 
 
+VALU_MODES = {"exp_f32": 0, "exp_f16": 1, "fma_f32": 2}
+
+
 def run_probe(args) -> int:
     """The reference ceilings: a register-only stream of v_mfma_f32_32x32x16_f16
-    (four independent chains per wavefront, two wavefronts per SIMD), or one
-    streaming read of a device buffer (16 bytes per lane, grid-strided).
+    (four independent chains per wavefront, two wavefronts per SIMD), one
+    streaming read of a device buffer (16 bytes per lane, grid-strided), or
+    the issue rate of one vector instruction kind (eight independent chains
+    per wavefront, four wavefronts per SIMD), in cycles per wave64
+    instruction per SIMD at the measured clock.
     Same timing as the workloads: warmup, then `--steps` launches between HIP
     events on the launch stream; clock and power sampled afterwards while the
     same launches run."""
@@ -217,7 +223,10 @@ def run_probe(args) -> int:
                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p,
                                          ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_valu_stream.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.fa_probe_mfma_stream.restype = lib.fa_probe_read_stream.restype = ctypes.c_int
+    lib.fa_probe_valu_stream.restype = ctypes.c_int
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -233,6 +242,17 @@ def run_probe(args) -> int:
                                         stream.cuda_stream) != 0:
                 raise RuntimeError("fa_probe_mfma_stream rejected")
         name, unit, peak = f"mfma_stream_f16_{args.mfma_probe}", "TFLOP/s", PEAK_FP16_TFLOPS
+    elif args.valu_probe:
+        workgroups, iters = 4 * cus, 2000  # two rounds of two 8-wavefront workgroups per CU
+        mode = VALU_MODES[args.valu_probe]
+        out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
+        work = workgroups * 8 * iters * 8.0  # wave64 instructions per launch
+
+        def step():
+            if lib.fa_probe_valu_stream(out.data_ptr(), out.numel(), workgroups, iters, mode,
+                                        stream.cuda_stream) != 0:
+                raise RuntimeError("fa_probe_valu_stream rejected")
+        name, unit, peak = f"valu_stream_{args.valu_probe}", "instr/ns", None
     else:
         nbytes = args.read_probe_mib * (1 << 20)
         buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
@@ -258,14 +278,20 @@ def run_probe(args) -> int:
     ms = t0.elapsed_time(t1) / args.steps
     rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
     result = {"probe": name, "value": round(rate, 1), "unit": unit, "peak": peak,
-              "frac_of_peak": round(rate / peak, 4), "ms_per_launch": round(ms, 4),
+              "frac_of_peak": round(rate / peak, 4) if peak else None, "ms_per_launch": round(ms, 4),
               "steps": args.steps, "warmup": args.warmup, "compute_units": cus,
               "workgroups": workgroups}
     if args.mfma_probe:
         result["flops_per_launch"] = work
+    elif args.valu_probe:
+        result["instructions_per_launch"] = work
+        result["ns_per_instruction_per_simd"] = round(ms * 1e6 / (work / (4 * cus)), 4)
     else:
         result["bytes_per_launch"] = int(work)
     clock = sample_clock_power(step)
+    if clock and args.valu_probe and (clock["gfxclk_mhz"] or 0) >= 500:
+        result["cycles_per_instruction_per_simd"] = round(
+            result["ns_per_instruction_per_simd"] * clock["gfxclk_mhz"] / 1000.0, 2)
     if clock and unit == "TFLOP/s" and (clock["gfxclk_mhz"] or 0) >= 500:
         clock["peak_at_clock_tflops"] = round(peak * clock["gfxclk_mhz"] / 2400.0, 1)
         clock["frac_at_clock"] = round(rate / clock["peak_at_clock_tflops"], 4)
@@ -290,6 +316,9 @@ def main() -> int:
                     help="instead of the benchmark, time the register-only fp16 MFMA stream of "
                          "libfa_clock.so on random operands (the sustained matrix-unit ceiling "
                          "for data like the workloads') or on few distinct small values")
+    ap.add_argument("--valu-probe", choices=sorted(VALU_MODES), default=None,
+                    help="instead of the benchmark, time a register-only stream of one vector "
+                         "instruction kind (libfa_clock.so): cycles per wave64 instruction per SIMD")
     ap.add_argument("--read-probe-mib", type=int, default=0,
                     help="instead of the benchmark, time a streaming read of this many MiB of "
                          "device memory (libfa_clock.so): the practical HBM read ceiling")
@@ -314,7 +343,7 @@ def main() -> int:
                           "launches": args.steps}), flush=True)
         return 0
 
-    if args.mfma_probe or args.read_probe_mib:
+    if args.mfma_probe or args.read_probe_mib or args.valu_probe:
         return run_probe(args)
 
     import tiled_attention_flash_amd as fa

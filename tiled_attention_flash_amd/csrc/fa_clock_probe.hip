@@ -1,8 +1,9 @@
 // fa_clock_probe.hip -- measurement helpers for the benchmark (libfa_clock.so),
-// not part of the attention library: the shader clock probe, and two
-// reference kernels that give the ceilings the attention kernels are judged
-// against on this part -- a register-only stream of fp16 matrix
-// instructions, and a streaming read of device memory.
+// not part of the attention library: the shader clock probe, and reference
+// kernels that give the ceilings the attention kernels are judged against
+// on this part -- a register-only stream of fp16 matrix instructions, a
+// streaming read of device memory, and the issue rate of the vector
+// instructions the softmax is made of.
 //
 // The shader clock the GPU actually runs at while a workload executes: one
 // wavefront, launched on a side stream while the workload's kernels are in
@@ -102,7 +103,60 @@ read_stream_kernel(const uint4p *buf, size_t n16, unsigned int *out)
     out[gid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// Vector-ALU issue rate of one instruction kind: eight independent chains per
+// wavefront of v_exp_f32 (mode 0), v_exp_f16 (mode 1) or v_fma_f32 (mode 2)
+// on registers, 512 threads per workgroup.  The chains stay bounded (x <-
+// 2^-x converges to about 0.64, x <- x/2 + 1/4 to 1/2), so no operand is ever
+// infinite or denormal.  Each thread writes one sum so the chains are kept.
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512))) void
+valu_stream_kernel(float *out, int iters, int mode)
+{
+    const int t = threadIdx.x;
+    float x[8];
+    _Float16 h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        x[i] = 1e-3f * (float)((t & 63) + i);
+        h[i] = (_Float16)x[i];
+    }
+    const float half_ = 0.5f, quarter = 0.25f;
+    if (mode == 0) {
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) __asm__ volatile("v_exp_f32 %0, -%0" : "+v"(x[i]));
+    } else if (mode == 1) {
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) __asm__ volatile("v_exp_f16 %0, -%0" : "+v"(h[i]));
+    } else {
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                __asm__ volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(half_), "v"(quarter));
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += x[i] + (float)h[i];
+    out[(size_t)blockIdx.x * blockDim.x + t] = s;
+}
+
 }  // namespace
+
+// Vector-ALU rate: `workgroups` workgroups of 512 threads, each wavefront
+// issuing 8 * iters instructions of the kind `mode` selects (0 v_exp_f32,
+// 1 v_exp_f16, 2 v_fma_f32).  out: device buffer of at least workgroups *
+// 512 floats.  Returns 0, or 1 on bad arguments or a rejected launch.
+extern "C" __attribute__((visibility("default"))) int fa_probe_valu_stream(void *out, long long out_floats,
+                                                                            int workgroups, int iters, int mode,
+                                                                            void *stream)
+{
+    if (!out || workgroups <= 0 || iters <= 0 || mode < 0 || mode > 2 ||
+        out_floats < (long long)workgroups * 512)
+        return 1;
+    hipLaunchKernelGGL(valu_stream_kernel, dim3(workgroups), dim3(512), 0, (hipStream_t)stream,
+                       (float *)out, iters, mode);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 
 // Matrix-unit ceiling: `workgroups` workgroups of 512 threads, each wavefront
 // issuing 32 * iters v_mfma_f32_32x32x16_f16 (32768 flops each); random
