@@ -70,9 +70,10 @@
 //   receive workgroups round-robin) walks a contiguous range of work items,
 //   keeping one head's K/V in that XCD's L2.
 // * Grid, causal: persistent, as the pages' kernel loops over q blocks -- the
-//   resident workgroups walk their XCD's range of units, each unit the pair
-//   of q blocks (nQ-1-i, i) of one row group, so every unit holds equal
-//   work and no workgroup is left with only diagonal-heavy blocks.
+//   resident workgroups walk their XCD's range of row groups in phases of a
+//   few row groups, taking single q blocks heaviest first in rounds of
+//   alternating direction, so that the work per workgroup evens out and no
+//   workgroup is left with only diagonal-heavy blocks (see run()).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
