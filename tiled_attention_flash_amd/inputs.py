@@ -93,6 +93,9 @@ WORKLOADS = {
     "mha-b8-h32-L1024-d64-causal": Workload("mha-b8-h32-L1024-d64-causal", 8, 32, 32, 1024, 64, True),
     "mha-b8-h32-L4096-d128": Workload("mha-b8-h32-L4096-d128", 8, 32, 32, 4096, 128, False),
     "mha-b8-h32-L4096-d128-causal": Workload("mha-b8-h32-L4096-d128-causal", 8, 32, 32, 4096, 128, True),
+    # the same tokens as B=8 L=4096 at half the length: the causal instance
+    # with four wavefronts per workgroup (fewer than 4096 keys)
+    "mha-b16-h32-L2048-d128-causal": Workload("mha-b16-h32-L2048-d128-causal", 16, 32, 32, 2048, 128, True),
     "gqa-b2-h32-kv8-L8192-d128-causal": Workload("gqa-b2-h32-kv8-L8192-d128-causal", 2, 32, 8, 8192, 128, True),
     "mha-b1-h32-L16384-d128-causal-qk3": Workload("mha-b1-h32-L16384-d128-causal-qk3", 1, 32, 32, 16384, 128, True, 3.0),
     # 1024 new queries after 3072 cached positions (a prefill continuing a prefix)
