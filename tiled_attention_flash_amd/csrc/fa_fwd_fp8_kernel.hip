@@ -493,18 +493,42 @@ struct Kernel8 {
         // O = v_descale * acc / l (guarded as on the page); LSE = scale' * m + ln(l / 2^3)
         const float lt = pair_sum(st.l);
         const float inv = a.v_descale / (lt > 1e-6f ? lt : 1.0f);
+        // Register 4rb+J of d block i holds d = 32i + 8rb + 4h + J.  For each
+        // pair rb = 2e, 2e+1 the lane halves swap one packed pair
+        // (v_permlane32_swap: the upper lanes of the first operand trade with
+        // the lower lanes of the second); then half 0 holds d = 32i+16e+0..7
+        // and half 1 d = 32i+16e+8..15, so every lane stores 16 contiguous
+        // bytes of its row.  Lanes l and l^32 share a row: every lane takes
+        // part in the exchange.
+        uint32_t ow[kDBlocks][2][4];
+#pragma unroll
+        for (int i = 0; i < kDBlocks; ++i)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                uint32_t w[2][2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int rb = 2 * e + j;
+                    const float2v lo2 = {st.oacc[i][4 * rb + 0] * inv, st.oacc[i][4 * rb + 1] * inv};
+                    const float2v hi2 = {st.oacc[i][4 * rb + 2] * inv, st.oacc[i][4 * rb + 3] * inv};
+                    w[j][0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo2, half2v));
+                    w[j][1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, half2v));
+                }
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(w[0][x], w[1][x], false, false);
+                    ow[i][e][x] = r[0];      // half 0: d +0..3, half 1: d +8..11
+                    ow[i][e][2 + x] = r[1];  // half 0: d +4..7, half 1: d +12..15
+                }
+            }
         if (qi < Lq) {
             _Float16 *orow = a.o + ((int64_t)b * Lq + qi) * a.H * D + (int64_t)hq * D;
 #pragma unroll
             for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const float2v lo2 = {st.oacc[i][4 * rb + 0] * inv, st.oacc[i][4 * rb + 1] * inv};
-                    const float2v hi2 = {st.oacc[i][4 * rb + 2] * inv, st.oacc[i][4 * rb + 3] * inv};
-                    const half2v hl = __builtin_convertvector(lo2, half2v);
-                    const half2v hh = __builtin_convertvector(hi2, half2v);
-                    const half4 out = {hl[0], hl[1], hh[0], hh[1]};
-                    *(half4 *)(orow + 32 * i + 8 * rb + 4 * h) = out;
+                for (int e = 0; e < 2; ++e) {
+                    const uint4v v4 = {ow[i][e][0], ow[i][e][1], ow[i][e][2], ow[i][e][3]};
+                    *(uint4v *)(orow + 32 * i + 16 * e + 8 * h) = v4;
                 }
             if (a.lse && h == 0)
                 a.lse[((int64_t)b * a.H + hq) * Lq + qi] = st.m * a.lse_scale + __logf(lt) - kOffsetLog2 * kLn2;
