@@ -45,12 +45,18 @@ _COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
 def kernel_sha(path: str = "forward") -> str:
     """Hash of the sources of one entry point's kernels (a workload's `path`),
     with comments and blank lines removed, so that an edit to comments alone
-    keeps the counters taken on the same code."""
+    keeps the counters taken on the same code, and of the extra compiler
+    flags the build gives those sources."""
+    from tiled_attention_flash_amd.build import SOURCE_FLAGS
+
     h = hashlib.sha256()
     for src in KERNEL_SRCS[path]:
         with open(src, encoding="utf-8") as f:
             code = _COMMENT.sub("", f.read())
         h.update("\n".join(line.rstrip() for line in code.splitlines() if line.strip()).encode())
+        flags = SOURCE_FLAGS.get(os.path.basename(src))
+        if flags:
+            h.update(("\nflags: " + " ".join(flags)).encode())
     return h.hexdigest()[:16]
 
 

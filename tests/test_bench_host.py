@@ -41,3 +41,17 @@ def test_kernel_hash_covers_each_paths_sources():
         names = [os.path.basename(s) for s in srcs]
         assert "fa_device.h" in names and "fa_internal.h" in names, path
         assert all(os.path.exists(s) for s in srcs), path
+
+
+def test_kernel_hash_covers_build_flags(monkeypatch):
+    """A change of the extra flags a kernel source is built with moves that
+    path's hash (the counters were taken on the code those flags produce)."""
+    from tiled_attention_flash_amd import build as fa_build
+
+    before = {p: bench.kernel_sha(p) for p in bench.KERNEL_SRCS}
+    flags = dict(fa_build.SOURCE_FLAGS)
+    flags["fa_bwd_kernel.hip"] = ["-mllvm", "-some-other-option"]
+    monkeypatch.setattr(fa_build, "SOURCE_FLAGS", flags)
+    after = {p: bench.kernel_sha(p) for p in bench.KERNEL_SRCS}
+    assert after["backward"] != before["backward"]
+    assert all(after[p] == before[p] for p in after if p != "backward")

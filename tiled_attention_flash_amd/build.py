@@ -6,9 +6,11 @@ direct load could read a wrong base address.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -23,6 +25,11 @@ HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibili
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["fa_host.cpp", "fa_fwd_kernel.hip", "fa_fwd_fp8_kernel.hip", "fa_splitkv_kernel.hip",
            "fa_bwd_kernel.hip"]
+# Extra flags per source.  The forward kernels are scheduled with LLVM's
+# max-ILP machine scheduler: +0.8 % on the B=8 H=32 L=4096 D=128 pass in two
+# same-process A/B runs (the fp8 kernel spills under it, so it keeps the
+# default).
+SOURCE_FLAGS = {"fa_fwd_kernel.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:
@@ -63,9 +70,24 @@ def check_assembly() -> None:
         raise RuntimeError("kernel assembly check failed:\n" + "\n".join(bad[:20]))
 
 
+def build_library(out: str = LIB) -> str:
+    """libfa.so from SOURCES, each compiled with its SOURCE_FLAGS, then linked."""
+    with tempfile.TemporaryDirectory() as tmp:
+        def compile_one(src):
+            obj = os.path.join(tmp, src + ".o")
+            _quiet_run([hipcc(), *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+                        os.path.join(CSRC, src), "-o", obj])
+            return obj
+        with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        _quiet_run([hipcc(), *HIP_FLAGS, "-shared", *objs, "-o", out + ".tmp"])
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build() -> str:
     build_shared([os.path.join(CSRC, "fa_clock_probe.hip")], CLOCK_LIB)
-    lib = build_shared([os.path.join(CSRC, s) for s in SOURCES], LIB, include_dirs=[INCLUDE, CSRC])
+    lib = build_library()
     check_assembly()
     return lib
 

@@ -36,10 +36,10 @@ VALU_SGPR_TO_VMEM_WAITS = 5
 
 
 def assemble(src: str, outdir: str) -> str:
-    """gfx950 assembly of one kernel source, built with the library's flags."""
+    """gfx950 assembly of one kernel source, built with the library's flags for it."""
     out = os.path.join(outdir, src + ".s")
-    cmd = [fa_build.hipcc(), *fa_build.HIP_FLAGS, f"-I{fa_build.INCLUDE}", f"-I{fa_build.CSRC}",
-           "--cuda-device-only", "-S", "-o", out, os.path.join(fa_build.CSRC, src)]
+    cmd = [fa_build.hipcc(), *fa_build.HIP_FLAGS, *fa_build.SOURCE_FLAGS.get(src, []), f"-I{fa_build.INCLUDE}",
+           f"-I{fa_build.CSRC}", "--cuda-device-only", "-S", "-o", out, os.path.join(fa_build.CSRC, src)]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"assembling {src} failed:\n{r.stdout}")
