@@ -33,9 +33,10 @@ PEAK_FP8_TFLOPS = 5033.2  # dense E4M3: twice the fp16 rate
 PEAK_HBM_GBS = 8000.0  # HBM3E, published
 CSRC = os.path.join(ROOT, "tiled_attention_flash_amd", "csrc")
 # the sources the kernels of each entry point are compiled from
-KERNEL_SRCS = {path: [os.path.join(CSRC, f) for f in ("fa_device.h", "fa_internal.h", src)]
-               for path, src in (("forward", "fa_fwd_kernel.hip"), ("splitkv", "fa_splitkv_kernel.hip"),
-                                 ("backward", "fa_bwd_kernel.hip"), ("fp8", "fa_fwd_fp8_kernel.hip"))}
+KERNEL_SRCS = {path: [os.path.join(CSRC, f) for f in ("fa_device.h", "fa_internal.h", *srcs)]
+               for path, srcs in (("forward", ("fa_fwd_kernel.hip",)), ("splitkv", ("fa_splitkv_kernel.hip",)),
+                                  ("backward", ("fa_bwd_kernels.h", "fa_bwd_kernel.hip", "fa_bwd_kernel_d64.hip")),
+                                  ("fp8", ("fa_fwd_fp8_kernel.hip",)))}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

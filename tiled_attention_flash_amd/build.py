@@ -24,12 +24,14 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fvisibility=hidden",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["fa_host.cpp", "fa_fwd_kernel.hip", "fa_fwd_fp8_kernel.hip", "fa_splitkv_kernel.hip",
-           "fa_bwd_kernel.hip"]
-# Extra flags per source.  The forward kernels are scheduled with LLVM's
-# max-ILP machine scheduler: +0.8 % on the B=8 H=32 L=4096 D=128 pass in two
-# same-process A/B runs (the fp8 kernel spills under it, so it keeps the
-# default).
-SOURCE_FLAGS = {"fa_fwd_kernel.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+           "fa_bwd_kernel.hip", "fa_bwd_kernel_d64.hip"]
+# Extra flags per source.  The forward kernels and the D = 64 backward
+# kernels are scheduled with LLVM's max-ILP machine scheduler (same-process
+# A/B: forward +0.8 % at B=8 H=32 L=4096 D=128; backward at D = 64 +3 %, +5 %
+# causal); the fp8 kernel spills under it and the D = 128 backward kernels
+# run 2 % slower, so they keep the default.
+_MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+SOURCE_FLAGS = {"fa_fwd_kernel.hip": _MAX_ILP, "fa_bwd_kernel_d64.hip": _MAX_ILP}
 
 
 def hipcc() -> str:

@@ -27,7 +27,8 @@ import subprocess
 
 from . import build as fa_build
 
-SOURCES = ["fa_fwd_kernel.hip", "fa_fwd_fp8_kernel.hip", "fa_splitkv_kernel.hip", "fa_bwd_kernel.hip"]
+SOURCES = ["fa_fwd_kernel.hip", "fa_fwd_fp8_kernel.hip", "fa_splitkv_kernel.hip", "fa_bwd_kernel.hip",
+           "fa_bwd_kernel_d64.hip"]
 
 DMA = re.compile(r"^\s*(global_load_lds_\w+)\s+(\S+),\s*(\S+)")
 PACKED_F32 = re.compile(r"^\s*v_pk_(fma|mul|add|mov)_f32\b")
