@@ -205,6 +205,7 @@ def cpu_baseline(w, q, k, v, target_s: float, descale=None):
 
 
 VALU_MODES = {"exp_f32": 0, "exp_f16": 1, "fma_f32": 2}
+MFMA_PROBE_MODES = {"random": 0, "structured": 1, "shared-b": 2, "low-bits": 3}
 
 
 def run_probe(args) -> int:
@@ -240,12 +241,12 @@ def run_probe(args) -> int:
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     if args.mfma_probe:
         workgroups, iters = 8 * cus, 512  # 8 rounds of one 8-wavefront workgroup per CU
-        structured = int(args.mfma_probe == "structured")
+        mode = MFMA_PROBE_MODES[args.mfma_probe]
         out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev)
         work = workgroups * 8 * iters * 32 * 32768.0  # flops per launch
 
         def step():
-            if lib.fa_probe_mfma_stream(out.data_ptr(), out.numel(), workgroups, iters, structured,
+            if lib.fa_probe_mfma_stream(out.data_ptr(), out.numel(), workgroups, iters, mode,
                                         stream.cuda_stream) != 0:
                 raise RuntimeError("fa_probe_mfma_stream rejected")
         name, unit, peak = f"mfma_stream_f16_{args.mfma_probe}", "TFLOP/s", PEAK_FP16_TFLOPS
@@ -319,10 +320,12 @@ def main() -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB "
                          "`--steps` times (the reference kernel for scaling HBM byte counters)")
-    ap.add_argument("--mfma-probe", choices=["random", "structured"], default=None,
+    ap.add_argument("--mfma-probe", choices=sorted(MFMA_PROBE_MODES), default=None,
                     help="instead of the benchmark, time the register-only fp16 MFMA stream of "
                          "libfa_clock.so on random operands (the sustained matrix-unit ceiling "
-                         "for data like the workloads') or on few distinct small values")
+                         "for data like the workloads'), on few distinct small values, on random "
+                         "operands with B shared by four consecutive MFMAs, or on random operands "
+                         "with the 5 low fraction bits zero")
     ap.add_argument("--valu-probe", choices=sorted(VALU_MODES), default=None,
                     help="instead of the benchmark, time a register-only stream of one vector "
                          "instruction kind (libfa_clock.so): cycles per wave64 instruction per SIMD")

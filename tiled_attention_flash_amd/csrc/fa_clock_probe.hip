@@ -37,13 +37,16 @@ typedef unsigned int uint4p __attribute__((ext_vector_type(4)));
 // two per SIMD (the occupancy of the attention kernels at D = 128): the
 // matrix unit's sustained fp16 rate with no memory traffic at all.  The
 // matrix unit's power, and so the clock the part holds under its power
-// limit, depends on the operand bits: by default every operand is an fp16
-// value with a random sign, a random 10-bit fraction and a magnitude in
-// [1/4, 4) (an xorshift stream per lane), and the four chains rotate through
-// eight such A and B fragments, as a kernel multiplying Gaussian data sees;
-// `structured` instead uses few distinct small values (many zeros), which
-// draws much less power.  Each thread writes one sum at the end so the
-// chains are not removed.
+// limit, depends on the operand bits.  Operand patterns (MODE):
+//   0  every operand an fp16 value with a random sign, a random 10-bit
+//      fraction and a magnitude in [1/4, 4) (an xorshift stream per lane);
+//      the four chains rotate through eight such A and B fragments, as a
+//      kernel multiplying Gaussian data sees;
+//   1  few distinct small values (many zeros);
+//   2  as 0, but four consecutive MFMAs share their B fragment (operand
+//      reuse between neighbouring instructions);
+//   3  as 0 with the 5 low fraction bits zero (fewer bits that toggle).
+// Each thread writes one sum at the end so the chains are not removed.
 __device__ __forceinline__ unsigned int xorshift(unsigned int &x)
 {
     x ^= x << 13;
@@ -52,38 +55,50 @@ __device__ __forceinline__ unsigned int xorshift(unsigned int &x)
     return x;
 }
 
+// sign, exponent 13..16 (2^-2 .. 2^1), fraction under `mask`: binary16 bits
+__device__ __forceinline__ _Float16 random_half(unsigned int &x, unsigned int mask)
+{
+    const unsigned int r = xorshift(x);
+    const unsigned short h =
+        (unsigned short)(((r >> 15) & 0x8000u) | ((13u + (r & 3u)) << 10) | ((r >> 2) & mask));
+    return __builtin_bit_cast(_Float16, h);
+}
+
+template <int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2))) void
-mfma_stream_kernel(float *out, int iters, int structured)
+mfma_stream_kernel(float *out, int iters)
 {
     const int t = threadIdx.x;
     half8p A[8], B[8];
     unsigned int x = 0x9e3779b9u ^ (unsigned int)((blockIdx.x * blockDim.x + t) * 2654435761u);
+    constexpr unsigned int kMask = MODE == 3 ? 0x3e0u : 0x3ffu;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if (structured) {
+            if constexpr (MODE == 1) {
                 A[j][i] = (_Float16)(((t + i + j) & 7) * 0.0625f);
                 B[j][i] = (_Float16)(((t * 3 + i + j) & 7) * 0.0625f);
             } else {
-                // sign, exponent 13..16 (2^-2 .. 2^1), fraction: binary16 bits
-                const unsigned int ra = xorshift(x), rb = xorshift(x);
-                const unsigned short ha = (unsigned short)(((ra >> 15) & 0x8000u) | ((13u + (ra & 3u)) << 10) |
-                                                           ((ra >> 2) & 0x3ffu));
-                const unsigned short hb = (unsigned short)(((rb >> 15) & 0x8000u) | ((13u + (rb & 3u)) << 10) |
-                                                           ((rb >> 2) & 0x3ffu));
-                A[j][i] = __builtin_bit_cast(_Float16, ha);
-                B[j][i] = __builtin_bit_cast(_Float16, hb);
+                A[j][i] = random_half(x, kMask);
+                B[j][i] = random_half(x, kMask);
             }
         }
     floatx16p c0 = {}, c1 = {}, c2 = {}, c3 = {};
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[j], B[j], c0, 0, 0, 0);
-            c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[j], B[(j + 3) & 7], c1, 0, 0, 0);
-            c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 5) & 7], B[j], c2, 0, 0, 0);
-            c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 2) & 7], B[(j + 6) & 7], c3, 0, 0, 0);
+            if constexpr (MODE == 2) {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[j], B[j], c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 3) & 7], B[j], c1, 0, 0, 0);
+                c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 5) & 7], B[j], c2, 0, 0, 0);
+                c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 2) & 7], B[j], c3, 0, 0, 0);
+            } else {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[j], B[j], c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[j], B[(j + 3) & 7], c1, 0, 0, 0);
+                c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 5) & 7], B[j], c2, 0, 0, 0);
+                c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[(j + 2) & 7], B[(j + 6) & 7], c3, 0, 0, 0);
+            }
         }
     }
     float s = 0.0f;
@@ -159,17 +174,26 @@ extern "C" __attribute__((visibility("default"))) int fa_probe_valu_stream(void 
 }
 
 // Matrix-unit ceiling: `workgroups` workgroups of 512 threads, each wavefront
-// issuing 32 * iters v_mfma_f32_32x32x16_f16 (32768 flops each); random
-// operands, or few distinct small values when `structured` is nonzero.  out:
+// issuing 32 * iters v_mfma_f32_32x32x16_f16 (32768 flops each) on the
+// operand pattern `mode` (0 random, 1 structured, 2 random with B shared by
+// four consecutive MFMAs, 3 random with the 5 low fraction bits zero).  out:
 // device buffer of at least workgroups * 512 floats.  Returns 0, or 1 on bad
 // arguments or a rejected launch.
 extern "C" __attribute__((visibility("default"))) int fa_probe_mfma_stream(void *out, long long out_floats,
                                                                             int workgroups, int iters,
-                                                                            int structured, void *stream)
+                                                                            int mode, void *stream)
 {
-    if (!out || workgroups <= 0 || iters <= 0 || out_floats < (long long)workgroups * 512) return 1;
-    hipLaunchKernelGGL(mfma_stream_kernel, dim3(workgroups), dim3(512), 0, (hipStream_t)stream,
-                       (float *)out, iters, structured);
+    if (!out || workgroups <= 0 || iters <= 0 || mode < 0 || mode > 3 ||
+        out_floats < (long long)workgroups * 512)
+        return 1;
+    const dim3 grid(workgroups), block(512);
+    hipStream_t s = (hipStream_t)stream;
+    switch (mode) {
+    case 0: hipLaunchKernelGGL(mfma_stream_kernel<0>, grid, block, 0, s, (float *)out, iters); break;
+    case 1: hipLaunchKernelGGL(mfma_stream_kernel<1>, grid, block, 0, s, (float *)out, iters); break;
+    case 2: hipLaunchKernelGGL(mfma_stream_kernel<2>, grid, block, 0, s, (float *)out, iters); break;
+    default: hipLaunchKernelGGL(mfma_stream_kernel<3>, grid, block, 0, s, (float *)out, iters); break;
+    }
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
