@@ -459,18 +459,20 @@ static void *bwd_worker(void *arg)
     return NULL;
 }
 
-/* Gradients of sum(O * dO) for the attention forward with sequence length
- * L (queries = keys, mask i >= j when causal): dq [B][L][H][D], dk and dv
- * [B][L][Hkv][D], all double.  q, k, v, dout are binary16 bits in the
- * forward's layouts (dout like q).  Work is split over (b, K/V head) among
- * `nthreads` threads (0 = all online cores); returns 0, or -1 on invalid
- * sizes. */
-int fa_oracle_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
-                  double *dq, double *dk, double *dv, int B, int L, int H, int Hkv, int D,
-                  int causal, double scale, int nthreads)
+/* Gradients of sum(O * dO) for queries and keys of different lengths:
+ * query row i sits at position i + past_len and, under the causal mask,
+ * keeps key j iff i + past_len >= j (past_len is ignored without the mask),
+ * as in fa_oracle_fwd_kv; a row that keeps no key has output 0 and
+ * contributes nothing.  dq [B][Lq][H][D], dk and dv [B][Lk][Hkv][D], all
+ * double.  q, k, v, dout are binary16 bits in the forward's layouts (dout
+ * like q).  Work is split over (b, K/V head) among `nthreads` threads (0 =
+ * all online cores); returns 0, or -1 on invalid sizes. */
+int fa_oracle_bwd_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                     double *dq, double *dk, double *dv, int B, int Lq, int Lk, int H, int Hkv, int D,
+                     int causal, int past_len, double scale, int nthreads)
 {
-    if (check_problem(B, L, L, H, Hkv, D)) return -1;
-    problem_t p = {q, k, v, B, L, L, H, Hkv, D, causal ? 1 : 0, 0, scale};
+    if (check_problem(B, Lq, Lk, H, Hkv, D)) return -1;
+    problem_t p = {q, k, v, B, Lq, Lk, H, Hkv, D, causal ? 1 : 0, causal ? past_len : 0, scale};
     bwd_job_t job;
     memset(&job, 0, sizeof(job));
     job.p = &p;
@@ -479,7 +481,7 @@ int fa_oracle_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
     job.dk = dk;
     job.dv = dv;
     job.n_items = (long)B * Hkv;
-    if (job.n_items <= 0 || L == 0) return 0;
+    if (job.n_items <= 0) return 0;
     int nt = resolve_threads(nthreads);
     if (nt > job.n_items) nt = (int)job.n_items;
     pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
@@ -489,6 +491,15 @@ int fa_oracle_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
     pthread_mutex_destroy(&job.lock);
     free(tid);
     return 0;
+}
+
+/* The same with sequence length L for queries and keys (mask i >= j when
+ * causal): dq [B][L][H][D], dk and dv [B][L][Hkv][D]. */
+int fa_oracle_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                  double *dq, double *dk, double *dv, int B, int L, int H, int Hkv, int D,
+                  int causal, double scale, int nthreads)
+{
+    return fa_oracle_bwd_kv(q, k, v, dout, dq, dk, dv, B, L, L, H, Hkv, D, causal, 0, scale, nthreads);
 }
 
 /* ---------------------------------------------------------------- fp8 */

@@ -63,6 +63,9 @@ def _bind(path: str):
     lib.fa_oracle_bwd.argtypes = ([u16p, u16p, u16p, u16p, f64p, f64p, f64p] + [c_int] * 6 +
                                   [c_double, c_int])
     lib.fa_oracle_bwd.restype = c_int
+    lib.fa_oracle_bwd_kv.argtypes = ([u16p, u16p, u16p, u16p, f64p, f64p, f64p] + [c_int] * 8 +
+                                     [c_double, c_int])
+    lib.fa_oracle_bwd_kv.restype = c_int
     u8p = ctypes.POINTER(ctypes.c_uint8)
     lib.fa_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.fa_oracle_e4m3_to_double.restype = c_double
@@ -200,26 +203,27 @@ def row_probs(q, k, v, b: int, h: int, i: int, causal: bool = False, scale: floa
 
 
 def backward(q, k, v, dout, causal: bool = False, scale: float | None = None, nthreads: int = 0,
-             lib=None):
-    """Gradients of sum(O * dout) in fp64 for equal query and key lengths.
-    q, dout [B, L, H, D], k, v [B, L, Hkv, D] (float16).  Returns
-    (dq [B,L,H,D], dk [B,L,Hkv,D], dv [B,L,Hkv,D]) as float64 arrays."""
+             lib=None, past_len: int | None = None):
+    """Gradients of sum(O * dout) in fp64.  q, dout [B, Lq, H, D], k, v
+    [B, Lk, Hkv, D] (float16); under the causal mask query row i sits at
+    position i + past_len (default Lk - Lq) and keeps key j iff
+    i + past_len >= j, as in `forward`.  Returns (dq [B,Lq,H,D],
+    dk [B,Lk,Hkv,D], dv [B,Lk,Hkv,D]) as float64 arrays."""
     lib = lib or _load()
     q, k, v, B, Lq, Lk, H, Hkv, D = _shape(q, k, v)
     do = _as_half_bits(dout)
-    if Lq != Lk:
-        raise ValueError("the backward oracle takes equal query and key lengths")
     if do.shape != q.shape:
         raise ValueError(f"dout {do.shape} must be shaped like q {q.shape}")
     scale = default_scale(D) if scale is None else float(scale)
+    past = default_past_len(Lq, Lk) if past_len is None else int(past_len)
     dq = np.empty((B, Lq, H, D), np.float64)
     dk = np.empty((B, Lk, Hkv, D), np.float64)
     dv = np.empty((B, Lk, Hkv, D), np.float64)
-    rc = lib.fa_oracle_bwd(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-                           _ptr(v, ctypes.c_uint16), _ptr(do, ctypes.c_uint16),
-                           _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
-                           _ptr(dv, ctypes.c_double), B, Lq, H, Hkv, D, int(bool(causal)), scale,
-                           int(nthreads))
+    rc = lib.fa_oracle_bwd_kv(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                              _ptr(v, ctypes.c_uint16), _ptr(do, ctypes.c_uint16),
+                              _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                              _ptr(dv, ctypes.c_double), B, Lq, Lk, H, Hkv, D, int(bool(causal)),
+                              past, scale, int(nthreads))
     if rc:
         raise ValueError("oracle rejected the problem")
     return dq, dk, dv

@@ -10,7 +10,12 @@ Each pin checks oracle.backward against something other than itself:
   every key, or every value, by one common vector leaves all gradients
   unchanged; under the causal mask query row 0 gets dQ = 0 exactly;
 * grouped-query heads equal multi-head attention with K/V repeated and the
-  repeated heads' dK, dV summed; the thread count changes nothing.
+  repeated heads' dK, dV summed; the thread count changes nothing;
+* query and key lengths that differ, with the causal position offset
+  past_len: torch autograd in float64 through the plain masked softmax
+  (rows that keep no key have output 0); the last Lq rows of a square causal
+  problem whose other rows carry dO = 0; rows before the first key (negative
+  past_len) have dQ = 0 and change nothing else.
 Plausible mistakes planted in copies of the C source must each fail a pin.
 """
 from __future__ import annotations
@@ -147,8 +152,85 @@ def pin_threads(lib):
         assert np.array_equal(x, y)
 
 
+def torch_grads_kv(q, k, v, do, causal, scale, past):
+    """Reference gradients for Lq != Lk from torch autograd in float64 through
+    the plain definition: masked scores, softmax over the kept keys (a row
+    that keeps none has output 0), weighted sum of V."""
+    Lq, Lk = q.shape[1], k.shape[1]
+    g = q.shape[2] // k.shape[2]
+    Q, K, V = [t.double().permute(0, 2, 1, 3).contiguous().requires_grad_(True) for t in (q, k, v)]
+    DO = do.double().permute(0, 2, 1, 3)
+    keep = torch.ones(Lq, Lk, dtype=torch.bool)
+    if causal:
+        keep = torch.arange(Lq)[:, None] + past >= torch.arange(Lk)[None, :]
+    s = torch.matmul(Q, K.repeat_interleave(g, dim=1).transpose(-1, -2)) * scale
+    s = s.masked_fill(~keep, float("-inf"))
+    m = s.amax(dim=-1, keepdim=True)
+    m = torch.where(torch.isfinite(m), m, torch.zeros_like(m)).detach()
+    p = torch.exp(s - m)
+    z = p.sum(dim=-1, keepdim=True)
+    O = torch.matmul(p / torch.where(z > 0, z, torch.ones_like(z)), V.repeat_interleave(g, dim=1))
+    O.backward(DO)
+    return [t.grad.permute(0, 2, 1, 3).numpy() for t in (Q, K, V)]
+
+
+BWD_KV_CASES = [  # B, Lq, Lk, H, Hkv, D, past_len (None: Lk - Lq)
+    (1, 5, 17, 2, 1, 16, None),
+    (2, 13, 7, 4, 2, 32, None),    # more queries than keys
+    (1, 9, 25, 2, 2, 64, -4),      # the first 4 rows keep no key
+    (1, 6, 20, 4, 1, 8, 100),      # every key kept
+    (1, 33, 40, 2, 2, 128, 3),
+]
+
+
+def pin_autograd_kv(lib):
+    for n, (B, Lq, Lk, H, Hkv, D, past) in enumerate(BWD_KV_CASES):
+        q, _, _, do = make_qkvdo(B, Lq, H, Hkv, D, seed=500 + n)
+        _, k, v, _ = make_qkvdo(B, Lk, H, Hkv, D, seed=600 + n)
+        pl = Lk - Lq if past is None else past
+        scale = 1.0 / np.sqrt(D)
+        for causal in (False, True):
+            got = oracle.backward(q, k, v, do, causal=causal, past_len=past, lib=lib)
+            ref = torch_grads_kv(q, k, v, do, causal, scale, pl if causal else 0)
+            for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+                err = np.max(np.abs(g - r))
+                assert err <= TOL * max(1.0, np.max(np.abs(r))), (n, causal, name, err)
+
+
+def pin_prefix_kv(lib):
+    """Causal rows placed after a cached prefix (past_len = Lk - Lq) have the
+    gradients of the last Lq rows of the square causal problem over all Lk
+    positions in which the first Lk - Lq rows carry dO = 0 (those rows then
+    add nothing to dK and dV)."""
+    B, L, H, Hkv, D = 2, 29, 4, 2, 32
+    q, k, v, do = make_qkvdo(B, L, H, Hkv, D, seed=700)
+    for Lq in (1, 11, 29):
+        do_full = do.clone()
+        do_full[:, :L - Lq] = 0
+        dq_f, dk_f, dv_f = oracle.backward(q, k, v, do_full, causal=True, lib=lib)
+        dq, dk, dv = oracle.backward(q[:, L - Lq:].contiguous(), k, v, do[:, L - Lq:].contiguous(),
+                                     causal=True, lib=lib)
+        for a, b in ((dq, dq_f[:, L - Lq:]), (dk, dk_f), (dv, dv_f)):
+            assert np.max(np.abs(a - b)) <= TOL * max(1.0, np.max(np.abs(b))), Lq
+
+
+def pin_rows_before_first_key(lib):
+    """With past_len = -c (c > 0) the first c rows keep no key: their dQ is 0,
+    and the rest equals the problem without those rows at past_len = 0."""
+    B, Lq, Lk, H, Hkv, D, c = 1, 12, 15, 2, 1, 64, 5
+    q, _, _, do = make_qkvdo(B, Lq, H, Hkv, D, seed=710)
+    _, k, v, _ = make_qkvdo(B, Lk, H, Hkv, D, seed=711)
+    dq, dk, dv = oracle.backward(q, k, v, do, causal=True, past_len=-c, lib=lib)
+    assert np.all(dq[:, :c] == 0.0)
+    dq2, dk2, dv2 = oracle.backward(q[:, c:].contiguous(), k, v, do[:, c:].contiguous(), causal=True,
+                                    past_len=0, lib=lib)
+    for a, b in ((dq[:, c:], dq2), (dk, dk2), (dv, dv2)):
+        assert np.max(np.abs(a - b)) <= TOL * max(1.0, np.max(np.abs(b)))
+
+
 PINS = [pin_autograd, pin_finite_differences, pin_zero_dout, pin_sums, pin_shift_invariance,
-        pin_causal_row0, pin_gqa_equals_repeated, pin_threads]
+        pin_causal_row0, pin_gqa_equals_repeated, pin_threads, pin_autograd_kv, pin_prefix_kv,
+        pin_rows_before_first_key]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -170,6 +252,8 @@ MUTANTS = {
                   "acc += h2d(dout[q_index(p, b, i, h, d)]) * h2d(p->k[kv_index(p, b, j, hk, d)]);"),
     "group sum: last head only": ("            dk[kv_index(p, b, j, hk, d)] = 0.0;\n            dv[kv_index(p, b, j, hk, d)] = 0.0;\n        }\n    for (int h = hk * groups; h < (hk + 1) * groups; ++h) {",
                                   "            dk[kv_index(p, b, j, hk, d)] = 0.0;\n            dv[kv_index(p, b, j, hk, d)] = 0.0;\n        }\n    for (int h = (hk + 1) * groups - 1; h < (hk + 1) * groups; ++h) {"),
+    "unequal lengths: past_len dropped": ("problem_t p = {q, k, v, B, Lq, Lk, H, Hkv, D, causal ? 1 : 0, causal ? past_len : 0, scale};\n    bwd_job_t job;",
+                                          "problem_t p = {q, k, v, B, Lq, Lk, H, Hkv, D, causal ? 1 : 0, 0, scale};\n    bwd_job_t job;"),
     "dQ over masked keys": ("for (int j = 0; j < n; ++j) acc += dprob[j] * h2d(p->k[kv_index(p, b, j, hk, d)]);",
                             "for (int j = 0; j < n + (n < p->Lk); ++j) acc += (j < n ? dprob[j] : 1.0) * h2d(p->k[kv_index(p, b, j, hk, d)]);"),
 }
