@@ -275,6 +275,31 @@ FA_API int fa_bwd(const void *q, const void *k, const void *v, const void *o, co
                   const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int L,
                   int H, int Hkv, int D, int causal, float scale, hipStream_t stream);
 
+/*
+ * fa_bwd_kv -- the backward pass of fa_fwd_kv: queries and keys of
+ * different lengths (cross-attention; queries that follow past_len cached
+ * positions).  The same computation as fa_bwd, with query row i at position
+ * i + past_len among the keys: under the causal mask it keeps key j iff
+ * i + past_len >= j (past_len is ignored without the mask), exactly as in
+ * fa_fwd_kv.  A row that keeps no key has dq = 0 and adds nothing to dk and
+ * dv; a key that no row keeps gets dk = dv = 0.
+ *
+ * q, o, dout, dq   device pointers, fp16 [B][Lq][H][D]
+ * k, v, dk, dv     device pointers, fp16 [B][Lk][Hkv][D]
+ * lse, delta       device pointers, fp32 [B][H][Lq]
+ * B, Lq, Lk, H, Hkv, D, causal, past_len, scale, stream   as for fa_fwd_kv.
+ *
+ * Ownership and errors as for fa_bwd; the pointers a problem touches must be
+ * non-NULL (q, o, dout, lse, delta, dq when Lq > 0; k, v, dk, dv when
+ * Lk > 0).  B == 0, or Lq == Lk == 0, returns FA_OK and launches nothing;
+ * Lq == 0 with keys writes dk = dv = 0.  fa_bwd(..., L, ...) is
+ * fa_bwd_kv(..., L, L, ..., past_len = 0, ...).
+ */
+FA_API int fa_bwd_kv(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                     const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int Lq,
+                     int Lk, int H, int Hkv, int D, int causal, int past_len, float scale,
+                     hipStream_t stream);
+
 /* Human-readable name of an fa_status value (static storage, never NULL). */
 FA_API const char *fa_status_string(int status);
 

@@ -37,7 +37,7 @@ def test_library_loads_and_exports_header_symbols():
     names = declared_symbols()
     assert set(names) == {"fa_fwd", "fa_fwd_kv", "fa_fwd_fp8", "fa_fwd_splitkv",
                           "fa_fwd_splitkv_noalloc", "fa_splitkv_splits",
-                          "fa_splitkv_workspace_bytes", "fa_bwd", "fa_status_string",
+                          "fa_splitkv_workspace_bytes", "fa_bwd", "fa_bwd_kv", "fa_status_string",
                           "fa_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], check=True,
                          stdout=subprocess.PIPE, text=True).stdout
@@ -47,7 +47,7 @@ def test_library_loads_and_exports_header_symbols():
         assert hasattr(lib, n)
     # nothing beyond the declared C ABI leaks out of the library
     assert exported == set(names)
-    assert lib.fa_abi_version() == 6
+    assert lib.fa_abi_version() == 7
 
 
 def test_status_strings():
@@ -347,6 +347,40 @@ def test_bwd_empty_problems_are_noops():
     assert call_bwd(B=0, **nulls) == 0
     assert call_bwd(L=0, **nulls) == 0
     assert call_bwd(L=0, D=96) == 4
+
+
+BWD_KV_ARGS = dict(BWD_ARGS, Lq=100, Lk=300, past_len=200)
+del BWD_KV_ARGS["L"]
+
+
+def call_bwd_kv(**kw):
+    a = dict(BWD_KV_ARGS)
+    a.update(kw)
+    return fa.fa_bwd_kv(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["delta"], a["dq"],
+                        a["dk"], a["dv"], a["B"], a["Lq"], a["Lk"], a["H"], a["Hkv"], a["D"],
+                        a["causal"], a["past_len"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(dq=None), 1), (dict(k=None), 1), (dict(dv=None), 1),
+    (dict(Lq=-1), 2), (dict(Lk=-1), 2), (dict(Lk=(1 << 30) + 1), 2), (dict(past_len=(1 << 30) + 1), 2),
+    (dict(past_len=-(1 << 30) - 1), 2), (dict(H=4, Hkv=3), 3), (dict(D=32), 4), (dict(scale=-1.0), 5),
+    (dict(dk=DK + 4), 6), (dict(dq=Q), 7), (dict(dk=DV), 7),
+    # rows with no keys need no k, v, dk, dv -- but q-side pointers are still required
+    (dict(Lk=0, k=None, v=None, dk=None, dv=None, lse=None), 1),
+    # keys with no rows need no q-side pointers -- but k-side pointers are still required
+    (dict(Lq=0, q=None, o=None, dout=None, lse=None, delta=None, dq=None, dk=None), 1),
+])
+def test_bwd_kv_invalid_arguments_rejected_without_launch(kw, status):
+    assert call_bwd_kv(**kw) == status
+
+
+def test_bwd_kv_empty_problems_are_noops():
+    nulls = dict(q=None, k=None, v=None, o=None, dout=None, lse=None, delta=None, dq=None,
+                 dk=None, dv=None)
+    assert call_bwd_kv(B=0, **nulls) == 0
+    assert call_bwd_kv(Lq=0, Lk=0, **nulls) == 0
+    assert call_bwd_kv(Lq=0, Lk=0, D=96) == 4
 
 
 # ------------------------------------------------------------ fp8 forward ABI

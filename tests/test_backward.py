@@ -14,7 +14,10 @@ and every gradient finite.
 
 Cases: ragged lengths around the 32-row blocks and 64-key tiles, both head
 dimensions, causal and not; every grouped-query ratio; wide logits (Q, K x3);
-a non-default scale; the page's workload (B=8, H=32, L=1024, D=64) and the
+a non-default scale; queries and keys of different lengths (fa_bwd_kv:
+cross-attention, rows after a cached prefix, rows that see no key, keys
+that no row sees, no keys or no rows at all); the page's workload (B=8,
+H=32, L=1024, D=64) and the
 long B=8, H=32, L=4096, D=128 shape at full size, compared on whole
 (batch, K/V head) slices, which the oracle computes exactly because
 different slices do not interact; determinism; GQA equal to MHA with K/V
@@ -108,6 +111,62 @@ def test_backward_full_size_slices(B, L, H, Hkv, D, slices, causal):
         ref = oracle.backward(qs, ks, vs, dos, causal=causal)
         sub = (got[0][b:b + 1, :, hs], got[1][b:b + 1, :, hk:hk + 1], got[2][b:b + 1, :, hk:hk + 1])
         check(sub, ref, f"slice b={b} hk={hk}")
+
+
+def gpu_grads_kv(q, k, v, do, causal, past_len):
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.forward(qd, kd, vd, causal=causal, past_len=past_len)
+    dq, dk, dv, _ = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, past_len=past_len)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Lq,Lk,H,Hkv,D,past", [
+    (1, 77, 300, 4, 2, 128, None),     # cross-attention / rows after a 223-key prefix
+    (2, 300, 77, 2, 1, 64, None),      # more rows than keys (negative default offset)
+    (1, 70, 50, 4, 4, 128, -20),       # the first 20 rows see no key
+    (1, 33, 129, 2, 2, 64, 500),       # every key visible
+    (1, 129, 257, 8, 2, 128, 0),       # offset 0 with more keys: keys past row 128 unseen when causal
+    (2, 1, 333, 4, 1, 64, None),       # one row after 332 cached keys
+    (1, 1024, 4096, 4, 2, 128, None),  # a prefill of 1024 rows after 3072 cached keys
+])
+def test_backward_unequal_lengths(B, Lq, Lk, H, Hkv, D, past, causal):
+    q, _, _, do = make_qkvdo(B, Lq, H, Hkv, D, seed=1600 + Lq)
+    _, k, v, _ = make_qkvdo(B, Lk, H, Hkv, D, seed=1700 + Lk)
+    what = f"B{B} Lq{Lq} Lk{Lk} H{H} Hkv{Hkv} D{D} past={past} causal={causal}"
+    print(what, flush=True)
+    ref = oracle.backward(q, k, v, do, causal=causal, past_len=past)
+    got = gpu_grads_kv(q, k, v, do, causal, past)
+    check(got, ref, what)
+    # rows that see no key have dq = 0 exactly, keys that no row sees dk = dv = 0 exactly
+    pl = Lk - Lq if past is None else past
+    if causal:
+        for i in range(Lq):
+            if i + pl < 0:
+                assert torch.all(got[0][:, i] == 0), (what, i)
+        first_unseen = max(0, Lq - 1 + pl + 1)
+        if first_unseen < Lk:
+            assert torch.all(got[1][:, first_unseen:] == 0) and torch.all(got[2][:, first_unseen:] == 0)
+
+
+def test_backward_no_rows_or_no_keys():
+    """No query rows: dk = dv = 0.  No keys: every row sees nothing, dq = 0."""
+    B, H, Hkv, D = 2, 4, 2, 128
+    _, k, v, _ = make_qkvdo(B, 50, H, Hkv, D, seed=1800)
+    q = torch.empty(B, 0, H, D, dtype=torch.float16)
+    o = torch.empty_like(q).cuda()
+    lse = torch.empty(B, H, 0, dtype=torch.float32, device="cuda")
+    dq, dk, dv, _ = fa.backward(q.cuda(), k.cuda(), v.cuda(), o, lse, q.cuda(), causal=False)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
+    q, _, _, do = make_qkvdo(B, 40, H, Hkv, D, seed=1801)
+    k0 = torch.empty(B, 0, Hkv, D, dtype=torch.float16, device="cuda")
+    for causal in (False, True):
+        o, lse = fa.forward(q.cuda(), k0, k0, causal=causal)
+        dq, dk, dv, _ = fa.backward(q.cuda(), k0, k0, o, lse, do.cuda(), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
 
 
 def test_backward_deterministic_and_gqa_equals_repeated():

@@ -37,6 +37,7 @@ import os
 
 __all__ = ["forward", "forward_splitkv", "forward_splitkv_noalloc", "forward_fp8", "backward",
            "fa_fwd", "fa_fwd_kv", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_fwd_fp8", "fa_bwd",
+           "fa_bwd_kv",
            "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_status_string", "library",
            "library_path", "FaError", "STATUS"]
 
@@ -90,6 +91,8 @@ def library():
     lib.fa_fwd_fp8.restype = c_int
     lib.fa_bwd.argtypes = [vp] * 10 + [c_int] * 6 + [ctypes.c_float, vp]
     lib.fa_bwd.restype = c_int
+    lib.fa_bwd_kv.argtypes = [vp] * 10 + [c_int] * 8 + [ctypes.c_float, vp]
+    lib.fa_bwd_kv.restype = c_int
     lib.fa_status_string.argtypes = [c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -292,19 +295,28 @@ def fa_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, L, H, Hkv, D, causal, sc
                                 int(Hkv), int(D), int(bool(causal)), float(scale), stream))
 
 
+def fa_bwd_kv(q, k, v, o, dout, lse, delta, dq, dk, dv, B, Lq, Lk, H, Hkv, D, causal, past_len,
+              scale, stream) -> int:
+    """Direct call of the backward entry point for Lq != Lk; status returned unchanged."""
+    return int(library().fa_bwd_kv(q, k, v, o, dout, lse, delta, dq, dk, dv, int(B), int(Lq),
+                                   int(Lk), int(H), int(Hkv), int(D), int(bool(causal)),
+                                   int(past_len), float(scale), stream))
+
+
 def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
-             dq=None, dk=None, dv=None, delta=None):
+             dq=None, dk=None, dv=None, delta=None, past_len: int | None = None):
     """Gradients (dq, dk, dv) of sum(o * dout) for the forward that produced
-    o and lse from q, k, v (equal query and key lengths), on the current
-    stream.  Output and Delta buffers are allocated with torch unless given;
-    returns (dq, dk, dv, delta)."""
+    o and lse from q, k, v, on the current stream.  q, o, dout [B, Lq, H, D],
+    k, v [B, Lk, Hkv, D]; with Lq != Lk (or an explicit ``past_len``) query
+    row i sits at key position i + past_len, default Lk - Lq, as in
+    ``forward``.  Output and Delta buffers are allocated with torch unless
+    given; returns (dq, dk, dv, delta)."""
     import torch
 
     _check_qkv(q, k, v)
     B, L, H, D = q.shape
-    Hkv = k.shape[2]
-    if k.shape[1] != L:
-        raise ValueError("backward takes equal query and key lengths")
+    Lk, Hkv = k.shape[1], k.shape[2]
+    past = Lk - L if past_len is None else int(past_len)
     for name, t in (("o", o), ("dout", dout)):
         if (not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or t.shape != q.shape or
                 not t.is_contiguous() or t.device != q.device):
@@ -331,7 +343,10 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     ptrs = [t.data_ptr() or None for t in (q, k, v, o, dout, lse, delta, dq, dk, dv)]
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = fa_bwd(*ptrs, B, L, H, Hkv, D, causal, scale, stream)
+        if Lk == L and past == 0:
+            st = fa_bwd(*ptrs, B, L, H, Hkv, D, causal, scale, stream)
+        else:
+            st = fa_bwd_kv(*ptrs, B, L, Lk, H, Hkv, D, causal, past, scale, stream)
     if st != 0:
         raise FaError(st, fa_status_string(st))
     return dq, dk, dv, delta

@@ -22,13 +22,15 @@ int launch_backward(const BwdProblem &p, hipStream_t stream)
     a.dq = (_Float16 *)p.dq;
     a.dk = (_Float16 *)p.dk;
     a.dv = (_Float16 *)p.dv;
-    a.L = p.L;
+    a.Lq = p.Lq;
+    a.Lk = p.Lk;
+    a.past_len = p.causal ? p.past_len : 0;
     a.H = p.H;
     a.Hkv = p.Hkv;
     a.groups = p.H / p.Hkv;
     a.n_blocks_item = 0;
     a.n_items = 0;
-    a.n_rows = (int64_t)p.B * p.L * p.H;
+    a.n_rows = (int64_t)p.B * p.Lq * p.H;
     a.scale = p.scale;
     a.c = p.scale * bwd::kLog2e;
     if (p.D == 64) return bwd::launch_backward_d64(a, p.B, p.causal, stream);

@@ -169,10 +169,12 @@ struct BwdArgs {
     const float *lse;
     float *delta;
     _Float16 *dq, *dk, *dv;
-    int L, H, Hkv, groups;
+    int Lq, Lk;         // query rows, key rows
+    int past_len;       // position of query row 0 among the keys (causal only, else 0)
+    int H, Hkv, groups;
     int n_blocks_item;  // key blocks (dkdv) or query blocks (dq) per (b, head)
     int n_items;
-    int64_t n_rows;     // B * L * H (delta)
+    int64_t n_rows;     // B * Lq * H (delta)
     float scale, c;     // c = scale * log2(e)
 };
 
@@ -205,8 +207,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void fa_bwd_de
     for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
     if (row < a.n_rows && sub == 0) {
         const int64_t h = row % a.H, bi = row / a.H;
-        const int64_t i = bi % a.L, b = bi / a.L;
-        a.delta[(b * a.H + h) * a.L + i] = acc;
+        const int64_t i = bi % a.Lq, b = bi / a.Lq;
+        a.delta[(b * a.H + h) * a.Lq + i] = acc;
     }
 }
 
@@ -232,34 +234,35 @@ struct DkDv {
     __device__ __forceinline__ static void stage(const BwdArgs &a, int b, int h, int q0, Smem &sm, int P)
     {
         const int64_t row_stride = (int64_t)a.H * D;
-        const _Float16 *qb = a.q + (int64_t)b * a.L * row_stride + (int64_t)h * D;
-        const _Float16 *gb = a.dout + (int64_t)b * a.L * row_stride + (int64_t)h * D;
-        Load::issue(qb, row_stride, q0, a.L, sm.q[P]);
-        Load::issue(gb, row_stride, q0, a.L, sm.g[P]);
+        const _Float16 *qb = a.q + (int64_t)b * a.Lq * row_stride + (int64_t)h * D;
+        const _Float16 *gb = a.dout + (int64_t)b * a.Lq * row_stride + (int64_t)h * D;
+        Load::issue(qb, row_stride, q0, a.Lq, sm.q[P]);
+        Load::issue(gb, row_stride, q0, a.Lq, sm.g[P]);
         // LSE and Delta of the 32 rows, by direct loads of lanes 0..31 of
         // wave 0 (a load into VGPRs and an LDS store would wait for the
-        // tile loads just issued).  Rows past the end re-read row L-1; on
+        // tile loads just issued).  Rows past the end re-read row Lq-1; on
         // the one block per head that has such rows, wave 0 waits for its
         // loads and sets their LSE to +inf (probability 0), before the
         // barrier that precedes any read of the block.
         if (threadIdx.x < kBQ) {
-            const int i = q0 + (int)threadIdx.x < a.L ? q0 + (int)threadIdx.x : a.L - 1;
-            const int64_t r0 = ((int64_t)b * a.H + h) * a.L;  // row 0 of (b, h); 4 i < 2^32
+            const int i = q0 + (int)threadIdx.x < a.Lq ? q0 + (int)threadIdx.x : a.Lq - 1;
+            const int64_t r0 = ((int64_t)b * a.H + h) * a.Lq;  // row 0 of (b, h); 4 i < 2^32
             dma4((const char *)(a.lse + r0), (uint32_t)(4 * i), sm.lse[P]);
             dma4((const char *)(a.delta + r0), (uint32_t)(4 * i), sm.delta[P]);
-            if (q0 + kBQ > a.L) {
+            if (q0 + kBQ > a.Lq) {
                 __builtin_amdgcn_s_waitcnt(0);
-                if (q0 + (int)threadIdx.x >= a.L) sm.lse[P][threadIdx.x] = __builtin_huge_valf();
+                if (q0 + (int)threadIdx.x >= a.Lq) sm.lse[P][threadIdx.x] = __builtin_huge_valf();
             }
         }
     }
 
     // P and dS of one 32 x 32 block as fp16 B operands: P = exp2(c s -
-    // log2(e) LSE) for the visible (query, key) pairs, 0 elsewhere (rows
-    // past the last query have LSE = +inf), and dS = P (dP - Delta).
+    // log2(e) LSE) for the visible (query, key) pairs -- key < Lk and,
+    // causal, key <= query + past_len -- 0 elsewhere (rows past the last
+    // query have LSE = +inf), and dS = P (dP - Delta).
     __device__ __forceinline__ static void probs(const floatx16 &s, const floatx16 &dp, const float *lse,
-                                                 const float *delta, int q0, int key, int L, int half, float c,
-                                                 half8 (&pf)[2], half8 (&sf)[2])
+                                                 const float *delta, int q0, int key, int Lk, int past,
+                                                 int half, float c, half8 (&pf)[2], half8 (&sf)[2])
     {
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -271,7 +274,7 @@ struct DkDv {
                 const int r = 4 * I + J;
                 const int qi = q0 + 8 * I + 4 * half + J;
                 float p = exp2_fast(__builtin_fmaf(s[r], c, -kLog2e * l4[J]));
-                if ((CAUSAL && key > qi) || key >= L) p = 0.0f;
+                if ((CAUSAL && key > qi + past) || key >= Lk) p = 0.0f;
                 pv[J] = p;
                 dsv[J] = p * (dp[r] - d4[J]);
             }
@@ -302,7 +305,7 @@ struct DkDv {
         const int kb = item % a.n_blocks_item;
         const int rest = item / a.n_blocks_item;
         const int hk = rest % a.Hkv, b = rest / a.Hkv;
-        const int L = a.L;
+        const int Lq = a.Lq, Lk = a.Lk, past = a.past_len;
         const int k_wg = kb * 32 * W;                 // first key of the workgroup
         const int key = k_wg + 32 * wave + col;       // this lane's key
         const int64_t kv_stride = (int64_t)a.Hkv * D;
@@ -312,15 +315,15 @@ struct DkDv {
         // workgroup go to LDS once and are read as B operands per block
         half8 kf[kSteps];
         {
-            const _Float16 *kr = a.k + ((int64_t)b * L + key) * kv_stride + (int64_t)hk * D;
+            const _Float16 *kr = a.k + ((int64_t)b * Lk + key) * kv_stride + (int64_t)hk * D;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
                 half8 x = {};
-                if (key < L) x = *(const half8 *)(kr + 16 * s + 8 * half);
+                if (key < Lk) x = *(const half8 *)(kr + 16 * s + 8 * half);
                 kf[s] = x;
             }
-            TileLoad<D, W, 32 * W>::issue(a.v + (int64_t)b * L * kv_stride + (int64_t)hk * D, kv_stride,
-                                          k_wg, L, sm.v);
+            TileLoad<D, W, 32 * W>::issue(a.v + (int64_t)b * Lk * kv_stride + (int64_t)hk * D, kv_stride,
+                                          k_wg, Lk, sm.v);
         }
         const _Float16 *vt = sm.v + 32 * wave * D;
         floatx16 dk[kDBlocks], dv[kDBlocks];
@@ -332,10 +335,15 @@ struct DkDv {
         TileRead<D> tr;
         tr.init();
 
-        // query blocks: causal -> from the block holding the workgroup's
-        // first key (earlier queries see none of its keys)
-        const int n_qb = (L + kBQ - 1) / kBQ;
-        const int qb0 = CAUSAL ? k_wg / kBQ : 0;
+        // query blocks: causal -> from the block holding the first query
+        // that sees the workgroup's first key, row k_wg - past_len (earlier
+        // queries see none of its keys)
+        const int n_qb = (Lq + kBQ - 1) / kBQ;
+        int qb0 = 0;
+        if (CAUSAL) {
+            const int64_t first = (int64_t)k_wg - past;
+            qb0 = first <= 0 ? 0 : (first >= (int64_t)n_qb * kBQ ? n_qb : (int)(first / kBQ));
+        }
         const int per_head = n_qb - qb0;
         const int total = per_head * a.groups;
         const float c = a.c;
@@ -362,7 +370,7 @@ struct DkDv {
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(tr.row_frag(gt, st), tr.row_frag(vt, st), dp, 0, 0, 0);
                 }
                 half8 pf[2], sf[2];
-                probs(s, dp, sm.lse[P], sm.delta[P], q0, key, L, half, c, pf, sf);
+                probs(s, dp, sm.lse[P], sm.delta[P], q0, key, Lk, past, half, c, pf, sf);
                 // dV^T += dO^T.P, dK^T += Q^T.dS (A operands transposed)
 #pragma unroll
                 for (int cs = 0; cs < 2; ++cs)
@@ -376,9 +384,9 @@ struct DkDv {
 
         // dK = scale dK^T^T, dV = dV^T^T: lane holds key `key`, d = 32i +
         // 8(r/4) + 4*half + r%4
-        if (key < L) {
-            _Float16 *dkr = a.dk + ((int64_t)b * L + key) * kv_stride + (int64_t)hk * D;
-            _Float16 *dvr = a.dv + ((int64_t)b * L + key) * kv_stride + (int64_t)hk * D;
+        if (key < Lk) {
+            _Float16 *dkr = a.dk + ((int64_t)b * Lk + key) * kv_stride + (int64_t)hk * D;
+            _Float16 *dvr = a.dv + ((int64_t)b * Lk + key) * kv_stride + (int64_t)hk * D;
 #pragma unroll
             for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
@@ -427,7 +435,7 @@ struct Dq {
         const int rest2 = rest / a.groups;
         const int hk = rest2 % a.Hkv, b = rest2 / a.Hkv;
         const int h = hk * a.groups + g;
-        const int L = a.L;
+        const int Lq = a.Lq, Lk = a.Lk, past = a.past_len;
         const int q0 = qb * kBM;
         const int qi = q0 + 32 * wave + col;  // this lane's query row
         const int64_t q_stride = (int64_t)a.H * D, kv_stride = (int64_t)a.Hkv * D;
@@ -435,12 +443,12 @@ struct Dq {
         // Q and dO of this lane's row as MFMA B operands (rows past the end: zeros)
         half8 qf[kSteps], gf[kSteps];
         {
-            const _Float16 *qr = a.q + ((int64_t)b * L + qi) * q_stride + (int64_t)h * D;
-            const _Float16 *gr = a.dout + ((int64_t)b * L + qi) * q_stride + (int64_t)h * D;
+            const _Float16 *qr = a.q + ((int64_t)b * Lq + qi) * q_stride + (int64_t)h * D;
+            const _Float16 *gr = a.dout + ((int64_t)b * Lq + qi) * q_stride + (int64_t)h * D;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
                 half8 x = {}, y = {};
-                if (qi < L) {
+                if (qi < Lq) {
                     x = *(const half8 *)(qr + 16 * s + 8 * half);
                     y = *(const half8 *)(gr + 16 * s + 8 * half);
                 }
@@ -448,10 +456,11 @@ struct Dq {
                 gf[s] = y;
             }
         }
-        const int64_t srow = ((int64_t)b * a.H + h) * L + qi;
-        // rows past the end: LSE = +inf (probability 0), Delta = 0
-        const float nl = qi < L ? -kLog2e * a.lse[srow] : -__builtin_huge_valf();
-        const float dlt = qi < L ? a.delta[srow] : 0.0f;
+        const int64_t srow = ((int64_t)b * a.H + h) * Lq + qi;
+        // rows past the end: LSE = +inf (probability 0), Delta = 0; a row
+        // that sees no key (LSE = -inf) has every key masked below
+        const float nl = qi < Lq ? -kLog2e * a.lse[srow] : -__builtin_huge_valf();
+        const float dlt = qi < Lq ? a.delta[srow] : 0.0f;
         const float c = a.c;
 
         floatx16 dq[kDBlocks];
@@ -460,24 +469,25 @@ struct Dq {
         TileRead<D> tr;
         tr.init();
 
-        // keys the work item can see
-        int kv_end = L;
+        // keys the work item can see: all Lk, or (causal) up to the position
+        // of its last query row
+        int kv_end = Lk;
         if (CAUSAL) {
-            const int last = (q0 + kBM < L ? q0 + kBM : L) - 1;
-            kv_end = last + 1;
+            const int64_t last = (int64_t)(q0 + kBM < Lq ? q0 + kBM : Lq) - 1 + past;
+            kv_end = last < 0 ? 0 : (last < Lk - 1 ? (int)last + 1 : Lk);
         }
         const int n_tiles = (kv_end + kBN - 1) / kBN;
         if (n_tiles > 0) {
-            Load::issue(a.k + (int64_t)b * L * kv_stride + (int64_t)hk * D, kv_stride, 0, L, klds[0]);
-            Load::issue(a.v + (int64_t)b * L * kv_stride + (int64_t)hk * D, kv_stride, 0, L, vlds[0]);
+            Load::issue(a.k + (int64_t)b * Lk * kv_stride + (int64_t)hk * D, kv_stride, 0, Lk, klds[0]);
+            Load::issue(a.v + (int64_t)b * Lk * kv_stride + (int64_t)hk * D, kv_stride, 0, Lk, vlds[0]);
         }
         for (int t = 0; t < n_tiles; ++t) {
             const int P = t & 1;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (t + 1 < n_tiles) {
-                Load::issue(a.k + (int64_t)b * L * kv_stride + (int64_t)hk * D, kv_stride, kBN * (t + 1), L, klds[P ^ 1]);
-                Load::issue(a.v + (int64_t)b * L * kv_stride + (int64_t)hk * D, kv_stride, kBN * (t + 1), L, vlds[P ^ 1]);
+                Load::issue(a.k + (int64_t)b * Lk * kv_stride + (int64_t)hk * D, kv_stride, kBN * (t + 1), Lk, klds[P ^ 1]);
+                Load::issue(a.v + (int64_t)b * Lk * kv_stride + (int64_t)hk * D, kv_stride, kBN * (t + 1), Lk, vlds[P ^ 1]);
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -500,7 +510,7 @@ struct Dq {
                     for (int e = 0; e < 2; ++e) {
                         const int kj = k0 + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
                         float p = exp2_fast(__builtin_fmaf(s[r + e], c, nl));
-                        if ((CAUSAL && kj > qi) || kj >= L) p = 0.0f;
+                        if ((CAUSAL && kj > qi + past) || kj >= Lk) p = 0.0f;
                         d2[e] = p * (dp[r + e] - dlt);
                     }
                     const float2v f2 = {d2[0], d2[1]};
@@ -518,8 +528,8 @@ struct Dq {
         }
 
         // dQ = scale (dQ^T)^T: lane holds row qi, d = 32i + 8(r/4) + 4*half + r%4
-        if (qi < L) {
-            _Float16 *dqr = a.dq + ((int64_t)b * L + qi) * q_stride + (int64_t)h * D;
+        if (qi < Lq) {
+            _Float16 *dqr = a.dq + ((int64_t)b * Lq + qi) * q_stride + (int64_t)h * D;
 #pragma unroll
             for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
@@ -546,8 +556,10 @@ int launch_bwd(BwdArgs a, int B, hipStream_t stream)
     {
         const int64_t blocks = (a.n_rows + 15) / 16;
         if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
-        hipLaunchKernelGGL((fa_bwd_delta<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-        if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+        if (blocks > 0) {
+            hipLaunchKernelGGL((fa_bwd_delta<D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+            if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+        }
     }
     // dK, dV
     {
@@ -555,23 +567,27 @@ int launch_bwd(BwdArgs a, int B, hipStream_t stream)
         // pass at D = 128, four otherwise (measured per workload)
         constexpr int W = (D == 128 && !CAUSAL) ? 8 : 4;
         BwdArgs b = a;
-        b.n_blocks_item = (a.L + 32 * W - 1) / (32 * W);
+        b.n_blocks_item = (a.Lk + 32 * W - 1) / (32 * W);
         const int64_t items = (int64_t)B * a.Hkv * b.n_blocks_item;
         if (items > 0x7fffffff) return FA_ERR_SHAPE;
         b.n_items = (int)items;
-        hipLaunchKernelGGL((fa_bwd_dkdv<D, CAUSAL, W>), dim3(b.n_items), dim3(64 * W), 0, stream, b);
-        if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+        if (items > 0) {  // none without keys
+            hipLaunchKernelGGL((fa_bwd_dkdv<D, CAUSAL, W>), dim3(b.n_items), dim3(64 * W), 0, stream, b);
+            if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+        }
     }
     // dQ
     {
         constexpr int W = (CAUSAL || D == 64) ? 4 : 8;
         BwdArgs b = a;
-        b.n_blocks_item = (a.L + 32 * W - 1) / (32 * W);
+        b.n_blocks_item = (a.Lq + 32 * W - 1) / (32 * W);
         const int64_t items = (int64_t)B * a.H * b.n_blocks_item;
         if (items > 0x7fffffff) return FA_ERR_SHAPE;
         b.n_items = (int)items;
-        hipLaunchKernelGGL((fa_bwd_dq<D, CAUSAL, W>), dim3(b.n_items), dim3(64 * W), 0, stream, b);
-        if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+        if (items > 0) {  // none without queries
+            hipLaunchKernelGGL((fa_bwd_dq<D, CAUSAL, W>), dim3(b.n_items), dim3(64 * W), 0, stream, b);
+            if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+        }
     }
     return FA_OK;
 }

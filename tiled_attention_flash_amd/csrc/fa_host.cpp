@@ -219,24 +219,31 @@ extern "C" int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *
     return fa::launch_splitkv(p, n_splits, scratch, stream);
 }
 
-extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
-                      const void *dout, const float *lse, float *delta, void *dq, void *dk,
-                      void *dv, int B, int L, int H, int Hkv, int D, int causal, float scale,
-                      hipStream_t stream)
+namespace {
+
+// Validation and dispatch of the backward entry points.  Every pointer a
+// nonempty problem reads or writes must be non-NULL: q, o, dout, lse, delta
+// and dq when there are query rows, k, v, dk and dv when there are keys.
+int backward(const void *q, const void *k, const void *v, const void *o, const void *dout,
+             const float *lse, float *delta, void *dq, void *dk, void *dv, int B, int Lq, int Lk,
+             int H, int Hkv, int D, int causal, int past_len, float scale, hipStream_t stream)
 {
-    if (B < 0 || L < 0 || H < 0 || Hkv < 0 || D < 0) return FA_ERR_SHAPE;
+    if (B < 0 || Lq < 0 || Lk < 0 || H < 0 || Hkv < 0 || D < 0) return FA_ERR_SHAPE;
     if (H <= 0 || Hkv <= 0 || H % Hkv != 0) return FA_ERR_GQA;
     if (D != 64 && D != 128) return FA_ERR_HEADDIM;
     if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
-    if (L > (1 << 30)) return FA_ERR_SHAPE;
-    const int64_t q_elems = elems4(B, L, H, D), kv_elems = elems4(B, L, Hkv, D);
-    const int64_t row_elems = elems4(B, H, L, 1);
+    // positions i + past_len and key indices stay far from int overflow
+    if (Lq > (1 << 30) || Lk > (1 << 30) || past_len > (1 << 30) || past_len < -(1 << 30))
+        return FA_ERR_SHAPE;
+    const int64_t q_elems = elems4(B, Lq, H, D), kv_elems = elems4(B, Lk, Hkv, D);
+    const int64_t row_elems = elems4(B, H, Lq, 1);
     if (q_elems < 0 || kv_elems < 0 || row_elems < 0 || q_elems > INT64_MAX / 4 ||
         kv_elems > INT64_MAX / 4)
         return FA_ERR_SHAPE;
-    if (B == 0 || L == 0) return FA_OK;
+    if (B == 0 || (Lq == 0 && Lk == 0)) return FA_OK;
 
-    if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA_ERR_NULLPTR;
+    if (Lq > 0 && (!q || !o || !dout || !lse || !delta || !dq)) return FA_ERR_NULLPTR;
+    if (Lk > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULLPTR;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
         misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
         misaligned(lse, 4) || misaligned(delta, 4))
@@ -254,8 +261,29 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o
         for (int j = i + 1; j < 4; ++j)
             if (overlaps(out[i], out_bytes[i], out[j], out_bytes[j])) return FA_ERR_ALIAS;
     }
-    fa::BwdProblem p{q, k, v, o, dout, lse, delta, dq, dk, dv, B, L, H, Hkv, D, causal != 0, scale};
+    fa::BwdProblem p{q, k, v, o, dout, lse, delta, dq, dk, dv, B, Lq, Lk, H, Hkv, D, causal != 0,
+                     causal ? past_len : 0, scale};
     return fa::launch_backward(p, stream);
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, float *delta, void *dq, void *dk,
+                      void *dv, int B, int L, int H, int Hkv, int D, int causal, float scale,
+                      hipStream_t stream)
+{
+    return backward(q, k, v, o, dout, lse, delta, dq, dk, dv, B, L, L, H, Hkv, D, causal, 0, scale,
+                    stream);
+}
+
+extern "C" int fa_bwd_kv(const void *q, const void *k, const void *v, const void *o,
+                         const void *dout, const float *lse, float *delta, void *dq, void *dk,
+                         void *dv, int B, int Lq, int Lk, int H, int Hkv, int D, int causal,
+                         int past_len, float scale, hipStream_t stream)
+{
+    return backward(q, k, v, o, dout, lse, delta, dq, dk, dv, B, Lq, Lk, H, Hkv, D, causal, past_len,
+                    scale, stream);
 }
 
 extern "C" const char *fa_status_string(int status)
@@ -282,4 +310,4 @@ extern "C" const char *fa_status_string(int status)
     }
 }
 
-extern "C" int fa_abi_version(void) { return 6; }
+extern "C" int fa_abi_version(void) { return 7; }

@@ -45,14 +45,16 @@ int launch_splitkv(const Problem &p, int n_splits, void *workspace, hipStream_t 
 constexpr int64_t kScratchBytes = FA_SPLITKV_SCRATCH_BYTES;
 int splitkv_scratch(void **ptr);
 
-// Validated backward problem (queries and keys equally long).
+// Validated backward problem.  Query row i sits at position i + past_len
+// among the keys (causal only; 0 otherwise).
 struct BwdProblem {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
     float *delta;
     void *dq, *dk, *dv;
-    int B, L, H, Hkv, D;
+    int B, Lq, Lk, H, Hkv, D;
     bool causal;
+    int past_len;
     float scale;
 };
 
