@@ -51,9 +51,10 @@
  * fp16*fp16 products, in double; exp/log are the C library's double routines.
  * Compiled without -ffast-math so the summation order is the one written.
  *
- * Backward pass (fa_oracle_bwd): the gradients of the scalar
- * sum_{b,i,h,d} O[b,i,h,d] * dO[b,i,h,d] with respect to Q, K and V, for
- * equal query and key lengths.  Page "TileLang 与机器学习训练：反向传播算子优化
+ * Backward pass (fa_oracle_bwd, fa_oracle_bwd_kv): the gradients of the
+ * scalar sum_{b,i,h,d} O[b,i,h,d] * dO[b,i,h,d] with respect to Q, K and V,
+ * for equal query and key lengths, or (fa_oracle_bwd_kv) for different
+ * lengths with the forward's position offset and mask.  Page "TileLang 与机器学习训练：反向传播算子优化
  * 案例", section "算子拆分与流水线设计", splits the computation into a
  * preprocess computing Delta from O and dO and a main kernel producing dQ,
  * dK and dV from Q, K, V, dO, lse and Delta; the section "反向传播算子的性能
