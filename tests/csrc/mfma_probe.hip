@@ -89,6 +89,24 @@ __global__ void mfma_f8_kernel(const int8v *a, const int8v *b, floatx16 *c, int 
         c[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], acc, 0, 0, 0, 0, 0, 0);
 }
 
+// n independent MFMAs, one wavefront each: block i takes its operands from
+// a[i], b[i] ([64 lanes][32 fp8 bytes]) and its accumulator input from
+// cin[i] ([64][16]), and writes c[i].  Unscaled form.
+__global__ void mfma_f8_batch_kernel(const int8v *a, const int8v *b, const floatx16 *cin, floatx16 *c)
+{
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    c[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[i], cin[i], 0, 0, 0, 0, 0, 0);
+}
+
+PROBE_API int probe_mfma_32x32x64_f8_batch(const void *a, const void *b, const void *cin, void *c, int n,
+                                           hipStream_t s)
+{
+    if (n <= 0) return 2;
+    hipLaunchKernelGGL(mfma_f8_batch_kernel, dim3(n), dim3(64), 0, s, (const int8v *)a, (const int8v *)b,
+                       (const floatx16 *)cin, (floatx16 *)c);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 // LDS[0..1023] = src; lane l reads 8 bytes with ds_read_b64_tr_b8 at byte
 // offset addr[l] (a multiple of 8, at most 1016: checked on the host).
 __global__ void tr8_kernel(const int *src, const int *addr, int2v *out)
