@@ -2,8 +2,9 @@
 computed on the CPU with the hardware's arithmetic, lies inside its buffer --
 for equal and for different query and key lengths (``fa_bwd_kv``).
 
-A model of the address arithmetic of ``fa_bwd_kernels.h`` (the staged tile
-loads of ``TileLoad::issue``, the LSE/Delta loads, the K, Q and dO row loads
+A model of the address arithmetic of ``fa_bwd_kernels.h`` (the Delta
+kernel's O and dO row reads and Delta stores, the staged tile loads of
+``TileLoad::issue``, the LSE/Delta loads, the K, Q and dO row loads
 and the gradient stores), written out again here; it must follow any change
 to that arithmetic.  As in the forward's model, a direct HBM -> LDS load adds
 the 64-bit scalar base (the tile's first row) and the 32-bit lane offset
@@ -69,8 +70,22 @@ def run_model(B, Lq, Lk, H, Hkv, D, causal, past_len):
         "k": Buf("k", 3 << 40, 2 * B * Lk * kvs), "v": Buf("v", 4 << 40, 2 * B * Lk * kvs),
         "lse": Buf("lse", 5 << 40, 4 * B * H * Lq), "delta": Buf("delta", 6 << 40, 4 * B * H * Lq),
         "dq": Buf("dq", 7 << 40, 2 * B * Lq * qs), "dk": Buf("dk", 8 << 40, 2 * B * Lk * kvs),
-        "dv": Buf("dv", 9 << 40, 2 * B * Lk * kvs),
+        "dv": Buf("dv", 9 << 40, 2 * B * Lk * kvs), "o": Buf("o", 10 << 40, 2 * B * Lq * qs),
     }
+    # Delta: one (b, i, h) row of O and dO per 16 lanes, rows in BSHD order
+    n_rows = B * Lq * H
+    blocks = (n_rows + 15) // 16
+    t = np.arange(256)
+    row = (np.arange(blocks)[:, None] * 16 + t[None, :] // 16).ravel()
+    sub = np.tile(t % 16, blocks)
+    live = row < n_rows
+    row, sub = row[live], sub[live]
+    per = D // 16
+    for name in ("o", "dout"):
+        bufs[name].check(bufs[name].base + 2 * (row * D + per * sub), 2 * per, f"delta {name}")
+    h, bi = row % H, row // H
+    i, bb = bi % Lq, bi // Lq
+    bufs["delta"].check(bufs["delta"].base + 4 * ((bb * H + h) * Lq + i), 4, "delta store")
     # dK, dV: items (b, hk, key block of 32 W keys)
     W = 8 if (D == 128 and not causal) else 4
     n_kb = (Lk + 32 * W - 1) // (32 * W)
