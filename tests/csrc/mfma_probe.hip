@@ -61,6 +61,23 @@ PROBE_API int probe_mfma_32x32x16_f16(const void *a, const void *b, void *c, hip
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
+// n independent f16 MFMAs, one wavefront each: block i takes a[i], b[i]
+// ([64 lanes][8 halves]) and the accumulator input cin[i] ([64][16]).
+__global__ void mfma_f16_batch_kernel(const half8 *a, const half8 *b, const floatx16 *cin, floatx16 *c)
+{
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    c[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[i], cin[i], 0, 0, 0);
+}
+
+PROBE_API int probe_mfma_32x32x16_f16_batch(const void *a, const void *b, const void *cin, void *c, int n,
+                                            hipStream_t s)
+{
+    if (n <= 0) return 2;
+    hipLaunchKernelGGL(mfma_f16_batch_kernel, dim3(n), dim3(64), 0, s, (const half8 *)a, (const half8 *)b,
+                       (const floatx16 *)cin, (floatx16 *)c);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 PROBE_API int probe_permlane32_swap(const void *x, void *out, hipStream_t s)
 {
     hipLaunchKernelGGL(permlane_kernel, dim3(1), dim3(64), 0, s, (const float *)x, (float *)out);

@@ -28,8 +28,10 @@ def load():
     lib.probe_cvt_fp8.argtypes = [vp, vp, ctypes.c_int, vp]
     lib.probe_mfma_4x4x4_16b_f16.argtypes = [vp, vp, vp, vp]
     lib.probe_mfma_32x32x64_f8_batch.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
+    lib.probe_mfma_32x32x16_f16_batch.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
     for f in (lib.probe_mfma_32x32x16_f16, lib.probe_permlane32_swap, lib.probe_cvt_f16,
               lib.probe_mfma_32x32x64_f8, lib.probe_ds_read_tr8, lib.probe_cvt_fp8,
-              lib.probe_mfma_4x4x4_16b_f16, lib.probe_mfma_32x32x64_f8_batch):
+              lib.probe_mfma_4x4x4_16b_f16, lib.probe_mfma_32x32x64_f8_batch,
+              lib.probe_mfma_32x32x16_f16_batch):
         f.restype = ctypes.c_int
     return lib
