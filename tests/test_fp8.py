@@ -39,7 +39,9 @@ Rows that see no key must be exactly O = 0 and LSE = -inf.
 Cases: ragged lengths around the 32-row blocks and 64-key tiles, both head
 dims, causal and not; every grouped-query ratio; wide logits (Q, K x3, which
 drive the probabilities deep into E4M3's subnormal range and exercise the
-overrun fixup); queries after cached keys (past_len, also negative); no keys;
+overrun fixup); the sum model's worst case (one large product and seven
+small ones just under the cut in every group of 8 d); queries after cached
+keys (past_len, also negative); no keys;
 descales far from 1; the two fp8 workloads at full size on sampled rows; and
 properties: determinism, LSE optional, argument errors.
 """
@@ -95,13 +97,14 @@ def score_slack(q8, k8, ds, scale, rows=None):
 
 
 def check_rows(o, lse, ro, rl, bound, absv, pv, delta, vmx, where=""):
-    """o, ro, bound, absv, pv: [n, D] rows; lse, rl, delta: [n]."""
+    """o, ro, bound, absv, pv: [n, D] rows; lse, rl, delta: [n].  Returns the
+    worst O error as a fraction of its bar and the largest |dLSE|."""
     seen = np.isfinite(rl)
     assert np.array_equal(np.isfinite(lse), seen), f"{where}: rows with no key differ"
     assert np.all(lse[~seen] == -np.inf), where
     assert np.all(o[~seen] == 0.0), where
     if not seen.any():
-        return 0.0
+        return 0.0, 0.0
     dl = np.abs(lse[seen] - rl[seen])
     worst_l = np.max(dl / (MAX_LSE + delta[seen]))
     assert worst_l <= 1.0, f"{where}: |dLSE| {worst_l:.3f} x its bar (max {dl.max():.3e})"
@@ -111,14 +114,19 @@ def check_rows(o, lse, ro, rl, bound, absv, pv, delta, vmx, where=""):
            + 2.0 ** -10 * np.abs(ro[seen]) + 1e-5 * vmx)
     worst = np.max(err / lim)
     assert worst <= 1.0, f"{where}: error {worst:.3f} x its bar"
-    return float(worst)
+    return float(worst), float(dl.max())
 
 
 def full_case(B, Lq, Lk, H, Hkv, D, causal, seed, mult=1.0, past_len=None, ds_mult=(1, 1, 1)):
     q8, k8, v8, ds = make_qkv_fp8(B, Lq, H, Hkv, D, seed=seed, qk_mult=mult, Lk=Lk)
     ds = tuple(d * m for d, m in zip(ds, ds_mult))
     past = Lk - Lq if past_len is None else past_len
-    scale = 1.0 / np.sqrt(D)
+    return compare_case(q8, k8, v8, ds, causal, 1.0 / np.sqrt(D), past,
+                        f"B={B} Lq={Lq} Lk={Lk} H={H} Hkv={Hkv} D={D} causal={causal} past={past}")
+
+
+def compare_case(q8, k8, v8, ds, causal, scale, past, where):
+    D = q8.shape[3]
     o, lse = run_gpu(q8, k8, v8, ds, causal, scale=scale, past_len=past)
     ro, rl, bound = oracle.forward_fp8(q8, k8, v8, ds, causal=causal, scale=scale, past_len=past,
                                        bound_model=MODEL)
@@ -130,8 +138,7 @@ def full_case(B, Lq, Lk, H, Hkv, D, causal, seed, mult=1.0, past_len=None, ds_mu
     # [B, Lq, H, D] and [B, H, Lq] -> rows (b, h, i)
     rows = lambda x: np.transpose(x, (0, 2, 1, 3)).reshape(-1, D)
     return check_rows(rows(o), lse.reshape(-1), rows(ro), rl.reshape(-1), rows(bound), rows(absv),
-                      rows(pv), delta.reshape(-1), vmax(v8, ds[2]),
-                      f"B={B} Lq={Lq} Lk={Lk} H={H} Hkv={Hkv} D={D} causal={causal} past={past}")
+                      rows(pv), delta.reshape(-1), vmax(v8, ds[2]), where)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -157,6 +164,43 @@ def test_fp8_wide_logits(D, causal):
 def test_fp8_queries_after_cached_keys(Lq, Lk, past):
     for causal in (False, True):
         full_case(1, Lq, Lk, 4, 2, 128, causal, seed=Lq + Lk, past_len=past)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_group_cut_worst_case(causal):
+    """Scores whose every group of 8 consecutive d holds one large product
+    (|q| = |k| = 16, sign random) and seven small positive ones just under
+    the group's cut (q = k = 0.171875: 0.0295 < 2^(8 - 13)): the matrix unit
+    drops all the small ones, about 3.3 raw units per score, the worst the
+    sum model allows within a factor 1.1.  The output must still meet the bar
+    whose score slack comes from that model."""
+    rng = np.random.default_rng(31)
+    B, L, H, Hkv, D = 1, 256, 2, 1, 128
+    big = np.zeros((D,), bool)
+    big[np.arange(0, D, 8) + rng.integers(0, 8, D // 8)] = True
+
+    def codes(n, heads):
+        x = np.full((B, n, heads, D), 0.171875, np.float32)
+        sgn = np.where(rng.random((B, n, heads, D)) < 0.5, -1.0, 1.0).astype(np.float32)
+        x[..., big] = 16.0 * sgn[..., big]
+        return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    q8, k8 = codes(L, H), codes(L, Hkv)
+    v8 = torch.from_numpy(rng.normal(size=(B, L, Hkv, D)).astype(np.float32) * 100).to(
+        torch.float8_e4m3fn).view(torch.uint8)
+    # raw scores are sums of 16 products of +-256; these descales bring the
+    # logits to a few units.  Every score of a row loses the same 3.3 raw
+    # units, so the LSE moves by about 4.6e-3 and O hardly at all: the LSE
+    # bar 1e-3 + delta holds only with the model's delta (2^-13 sum|p|
+    # would give 0.7e-3)
+    ds = (1.0 / 8, 1.0 / 8, 1.0 / 100)
+    scale = 1.0 / np.sqrt(D)
+    slack = score_slack(q8, k8, ds, scale)
+    assert slack.max() > 4e-3  # the case exercises the cut term
+    _, dlse = compare_case(q8, k8, v8, ds, causal, scale, 0, f"group-cut worst case causal={causal}")
+    # the kernel does drop the small products as the model says (a unit
+    # summing in fp32 would be within 1e-5 here)
+    assert dlse > 0.5 * 16 * 7 * 0.171875 ** 2 * scale * ds[0] * ds[1], dlse
 
 
 def test_fp8_no_keys():
